@@ -1,0 +1,193 @@
+/*
+ * psw.h - C ABI of libpsw.so: paged sliding-window attention with window-clamped
+ * image (multimodal-prefix) ranges on AMD Instinct MI355X (gfx950).
+ *
+ * The pages this library follows (cited by title and section):
+ *   [SWA-MM] vLLM PR #53147 summary (prhub.com.cn): sliding-window tile pruning
+ *            restored under a window-clamped multimodal-prefix mask.
+ *   [SLOT]   vllm-ascend Triton operator deep dive: _compute_slot_mapping_kernel
+ *            (0539edu.com): logical position -> physical KV-cache slot.
+ *   [DCP]    MLA DCP decode two-stream overlap and V-up fusion study notes,
+ *            vllm-ascend PR #16977: history/current partials merged by LSE.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers into memory the caller owns and keeps
+ *     alive until the enqueued work has finished. Arrays of pointers and the
+ *     argument struct itself are HOST memory, read before the call returns.
+ *   - `stream` is a hipStream_t (NULL: the legacy default stream). Every call
+ *     only enqueues work on it: no allocation, no host synchronisation.
+ *   - Scalars and pointer presence are validated on the host. On any error
+ *     nothing is enqueued and outputs are untouched. Device-resident data
+ *     (offsets, positions, table entries) is NOT validated; the preconditions
+ *     listed per call are the caller's to keep.
+ *   - All tensors are dense and row-major (last dimension contiguous).
+ *   - bf16 is IEEE bfloat16 (raw 16-bit patterns), fp32 is IEEE binary32.
+ */
+#ifndef PSW_H
+#define PSW_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PSW_ABI_VERSION 1
+
+enum psw_status {
+  PSW_OK = 0,
+  PSW_ERR_INVALID = -1,      /* bad scalar, missing pointer, inconsistent sizes */
+  PSW_ERR_UNSUPPORTED = -2,  /* valid request this build has no kernel for */
+  PSW_ERR_HIP = -3           /* a HIP launch failed; see psw_last_error() */
+};
+
+enum psw_dtype { PSW_BF16 = 0, PSW_F32 = 1 };
+
+/* Returns PSW_ABI_VERSION. */
+int psw_abi_version(void);
+
+/* Static text for a status code. */
+const char* psw_status_string(int status);
+
+/* Detail of the last error raised on the calling host thread ("" if none). */
+const char* psw_last_error(void);
+
+/*
+ * psw_slot_mapping - [SLOT] sections 1, 2, 4 and 5.1.
+ * For request r and every token t in [query_start_loc[r], query_start_loc[r+1]):
+ *     slot_mapping[t] = block_table[r * block_table_stride + pos / block_size] * block_size
+ *                       + pos % block_size,          pos = positions[t]
+ * and slot_mapping[t] = -1 (the pad slot id) for t in [num_tokens, max_num_tokens).
+ * A token whose position is negative, whose logical block is >= block_table_stride,
+ * or whose table entry is negative also gets -1.
+ *   query_start_loc   int32 [num_reqs + 1], non-decreasing, query_start_loc[0] = 0,
+ *                     query_start_loc[num_reqs] = num_tokens (device)
+ *   positions         int64 [num_tokens], values below 2^31 (device)
+ *   block_table       int32 [num_reqs, block_table_stride] (device)
+ *   slot_mapping      int32 [max_num_tokens] output (device)
+ * Errors: PSW_ERR_INVALID if num_reqs < 0, num_tokens < 0, block_table_stride < 1,
+ * block_size < 1, max_num_tokens < num_tokens, or a needed pointer is NULL.
+ */
+int psw_slot_mapping(const int32_t* query_start_loc, int32_t num_reqs,
+                     const int64_t* positions, int32_t num_tokens,
+                     const int32_t* block_table, int32_t block_table_stride,
+                     int32_t block_size, int32_t* slot_mapping, int32_t max_num_tokens,
+                     void* stream);
+
+/*
+ * psw_kv_cache_write - [SLOT] section 1 (the slot id addresses a token's K/V
+ * vector in the paged cache).  For every token t with slot s = slot_mapping[t] >= 0:
+ *     k_cache[s, h, :] = k_new[t, h, :]   and   v_cache[s, h, :] = v_new[t, h, :]
+ * Slots equal to -1 are skipped.
+ *   k_new    bf16 [num_tokens, num_kv_heads, head_dim_k]      (device)
+ *   v_new    bf16 [num_tokens, num_kv_heads, head_dim_v] or NULL (latent caches
+ *            keep V inside K; then v_cache must be NULL too)     (device)
+ *   k_cache  bf16 [num_slots, num_kv_heads, head_dim_k], slot = block * block_size
+ *            + offset, i.e. the [num_blocks, block_size, heads, dim] layout (device)
+ *   v_cache  bf16 [num_slots, num_kv_heads, head_dim_v] or NULL      (device)
+ * Preconditions: every slot_mapping[t] is -1 or in [0, num_slots); no two tokens
+ * share a slot.  head dims must be multiples of 8.
+ */
+int psw_kv_cache_write(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                       int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim_k,
+                       int32_t head_dim_v, void* k_cache, void* v_cache, int64_t num_slots,
+                       void* stream);
+
+/*
+ * Arguments of psw_swa_mm_attention and psw_tile_bounds.
+ *
+ * Mask ([SWA-MM] "Implementation breakdown" items 1-2, "Key source snippet",
+ * "Review highlights").  For request r, new token i has absolute position
+ * q = context_len + i with context_len = seq_lens[r] - query_len.  Key k in
+ * [0, seq_lens[r]) is allowed iff  base(q, k) OR image(q, k):
+ *   base, causal != 0:  q - window + 1 <= k <= q  (window <= 0: k <= q)
+ *   base, causal == 0:  |q - k| < window           (window <= 0: every key)
+ *   chunk_lookback >= 0 further restricts base to k >= ((q / chunk_size) - chunk_lookback) * chunk_size
+ *   image: some range [s, e] of the request (inclusive, absolute, used only when
+ *          s < e) holds both q and k, and k >= q - window + 1 (when window > 0).
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * Output row (token t, head h) = softmax(scale * q . k over allowed keys) . v,
+ * and lse = natural log of the sum of exp(scale * q . k) over those keys.
+ * A row with no allowed key (within its split) gets output 0 and lse -inf.
+ *
+ * Split-KV partials ([DCP] sections 1.1 and 3.1): with key_ranges != NULL, split j
+ * of request r only uses keys in [key_ranges[(j*num_seqs + r)*2], key_ranges[.. + 1]);
+ * begin >= end is an empty split.  Partials are written to out[j] and lse[j] and are
+ * merged afterwards with psw_lse_combine.
+ */
+typedef struct psw_attn_args {
+  int32_t struct_size;            /* = sizeof(psw_attn_args) */
+  const void* q;                  /* bf16 [num_tokens, num_q_heads, head_dim_qk] */
+  const void* k_cache;            /* bf16 [num_slots, num_kv_heads, head_dim_qk] */
+  const void* v_cache;            /* bf16 [num_slots, num_kv_heads, head_dim_v], or NULL:
+                                     V = first head_dim_v columns of k_cache (latent) */
+  const int32_t* block_table;     /* int32 [num_seqs, block_table_stride] */
+  const int32_t* query_start_loc; /* int32 [num_seqs + 1] */
+  const int32_t* seq_lens;        /* int32 [num_seqs], total keys incl. cached context */
+  const int32_t* mm_ranges;       /* int32 [num_seqs, max_mm_ranges, 2] or NULL (no images) */
+  const int32_t* key_ranges;      /* int32 [num_splits, num_seqs, 2] or NULL (one split) */
+  void* out;                      /* out_dtype [num_splits, num_tokens, num_q_heads, head_dim_v] */
+  float* lse;                     /* fp32 [num_splits, num_tokens, num_q_heads] or NULL */
+  int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v;
+  int32_t block_size, block_table_stride, max_mm_ranges;
+  int32_t window;                 /* > 0: sliding window; <= 0: none */
+  int32_t causal;                 /* 1: causal base; 0: bidirectional base */
+  int32_t chunk_size, chunk_lookback;  /* chunk_lookback < 0: off */
+  int32_t num_splits;             /* >= 1; must be 1 when key_ranges == NULL */
+  int32_t out_dtype;              /* PSW_BF16 or PSW_F32 */
+  float scale;                    /* softmax scale */
+} psw_attn_args;
+
+/*
+ * psw_swa_mm_attention - paged attention under the mask above, visiting only the
+ * KV tiles of each query block's union interval ([SWA-MM] "Key source snippet").
+ * Supported: (head_dim_qk, head_dim_v) in {(64,64), (128,128), (256,256)} with
+ * num_q_heads / num_kv_heads <= 128, and the latent decode shape (576, 512) with
+ * v_cache == NULL and one KV head.  block_size must be a power of two.
+ * Preconditions: query_start_loc non-decreasing from 0 to num_tokens;
+ * 1 <= query_len <= seq_len for every request with new tokens; block-table
+ * entries for every key below seq_len are valid blocks of the caches; image
+ * ranges lie in [0, seq_len).
+ * Errors: PSW_ERR_INVALID (struct_size mismatch, counts < 0, num_q_heads not a
+ * multiple of num_kv_heads, block_size not a power of two, chunk_size < 1 with
+ * chunk_lookback >= 0, num_splits < 1, num_splits > 1 without key_ranges, NULL
+ * pointer), PSW_ERR_UNSUPPORTED (head dims / dtype combination without a kernel).
+ */
+int psw_swa_mm_attention(const psw_attn_args* args, void* stream);
+
+/*
+ * psw_lse_combine - [DCP] "Terms", section 1.1 and code block D: merge P partial
+ * results row by row,  M = max_p lse_p,  w_p = exp(lse_p - M),
+ *     out = sum_p w_p * O_p / sum_p w_p,   out_lse = M + log(sum_p w_p).
+ * Partials with lse = -inf weigh 0; a row whose partials are all -inf gets 0 / -inf.
+ *   partial_out   host array of P device pointers, each partial_dtype [num_rows, head_dim_v]
+ *   partial_lse   host array of P device pointers, each fp32 [num_rows]
+ *   out           out_dtype [num_rows, head_dim_v] (device); out_lse fp32 [num_rows] or NULL
+ * The partials are read in place (no packing).  1 <= P <= 64; head_dim_v a
+ * multiple of 8 and at most 1024.
+ */
+int psw_lse_combine(const void* const* partial_out, const float* const* partial_lse,
+                    int32_t num_partials, int32_t partial_dtype, int64_t num_rows,
+                    int32_t head_dim_v, void* out, int32_t out_dtype, float* out_lse,
+                    void* stream);
+
+/*
+ * psw_tile_bounds - the per-query-block tile interval the attention kernel uses,
+ * exported for tests ([SWA-MM] "Key source snippet": the helper test kernel that
+ * calls the production bounds routine and stores its three results).
+ * For each query n: out[3n..3n+2] = (loop_lo, loop_hi, max_seq_prefix_len) of
+ * request seq_idx[n], query block q_block_idx[n] (rows q_block*block_q .. +
+ * (block_m - 1) / queries_per_kv), tiles of tile_size keys.  Uses geometry's
+ * query_start_loc, seq_lens, mm_ranges, max_mm_ranges, num_q_heads, num_kv_heads,
+ * window, causal, chunk_size, chunk_lookback; other fields are ignored.
+ *   seq_idx, q_block_idx  int32 [num_queries] (device);  out int32 [num_queries, 3] (device)
+ */
+int psw_tile_bounds(const psw_attn_args* geometry, int32_t tile_size, int32_t block_m,
+                    int32_t block_q, const int32_t* seq_idx, const int32_t* q_block_idx,
+                    int32_t num_queries, int32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSW_H */

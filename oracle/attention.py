@@ -57,17 +57,18 @@ def attention_ref(q, k, v, *, context_len, seq_len, scale, window, causal, chunk
         cols = np.nonzero(mask.any(axis=0))[0]
         if len(cols) == 0:
             continue
-        mask = mask[:, cols]
+        # rows of the score matrix: (new token, query head of the group), all
+        # query heads of one KV head stacked so one matmul serves the group
+        mask = np.repeat(mask[:, cols], qpk, axis=0)
         for g in range(hkv):
             K = np.asarray(k[cols, g], dtype=np.float64)
             V = np.asarray(v[cols, g], dtype=np.float64)
-            for h in range(g * qpk, (g + 1) * qpk):
-                Q = np.asarray(q[blk, h], dtype=np.float64)
-                S = scale * (Q @ K.T)
-                S[~mask] = -np.inf
-                o, l = _softmax_rows(S, V)
-                out[b0: b0 + len(blk), h] = o
-                lse[b0: b0 + len(blk), h] = l
+            Q = np.asarray(q[blk, g * qpk:(g + 1) * qpk], dtype=np.float64).reshape(-1, q.shape[2])
+            S = scale * (Q @ K.T)
+            S[~mask] = -np.inf
+            o, l = _softmax_rows(S, V)
+            out[b0: b0 + len(blk), g * qpk:(g + 1) * qpk] = o.reshape(len(blk), qpk, -1)
+            lse[b0: b0 + len(blk), g * qpk:(g + 1) * qpk] = l.reshape(len(blk), qpk)
     return out, lse
 
 

@@ -50,8 +50,9 @@ def allowed_rows(q_abs, seq_len, window, causal, chunk_size, chunk_lookback, ran
     if chunk_lookback >= 0:
         base = base & (k >= ((q // chunk_size) - chunk_lookback) * chunk_size)
     image = np.zeros_like(base)
+    q_min, q_max = (int(q.min()), int(q.max())) if q.size else (0, -1)
     for s, e in ranges:
-        if s < e:
+        if s < e and s <= q_max and e >= q_min:   # ranges no row lies in add nothing
             inr = (q >= s) & (q <= e) & (k >= s) & (k <= e)
             if window > 0:
                 inr = inr & (k >= q - window + 1)

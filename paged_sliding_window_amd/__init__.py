@@ -1,0 +1,14 @@
+"""Paged sliding-window attention with window-clamped image ranges for MI355X.
+
+Thin torch-facing marshalling over the C ABI of libpsw.so (include/psw.h):
+every step of the path runs in the library's HIP kernels; this module only
+checks tensor metadata and passes device pointers and the current stream.
+"""
+from .ops import (  # noqa: F401
+    kv_cache_write,
+    lse_combine,
+    slot_mapping,
+    swa_mm_attention,
+    tile_bounds,
+)
+from ._lib import LIB_PATH, PswError, load  # noqa: F401

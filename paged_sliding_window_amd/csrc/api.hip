@@ -1,0 +1,235 @@
+// extern "C" entry points of libpsw.so: host-side validation of scalars and
+// pointer presence, then one or more kernel launches on the caller's stream.
+// Nothing here allocates or synchronises.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <cstdarg>
+
+#include "../../include/psw.h"
+#include "device_common.h"
+#include "psw_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return PSW_OK;
+}
+
+int check_hip(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PSW_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+int log2i(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+int psw_abi_version(void) { return PSW_ABI_VERSION; }
+
+const char* psw_status_string(int status) {
+  switch (status) {
+    case PSW_OK: return "ok";
+    case PSW_ERR_INVALID: return "invalid argument";
+    case PSW_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PSW_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* psw_last_error(void) { return g_last_error; }
+
+int psw_slot_mapping(const int32_t* query_start_loc, int32_t num_reqs, const int64_t* positions,
+                     int32_t num_tokens, const int32_t* block_table, int32_t block_table_stride,
+                     int32_t block_size, int32_t* slot_mapping, int32_t max_num_tokens,
+                     void* stream) {
+  if (num_reqs < 0 || num_tokens < 0)
+    return fail(PSW_ERR_INVALID, "num_reqs (%d) and num_tokens (%d) must be >= 0", num_reqs,
+                num_tokens);
+  if (block_table_stride < 1 || block_size < 1)
+    return fail(PSW_ERR_INVALID, "block_table_stride (%d) and block_size (%d) must be >= 1",
+                block_table_stride, block_size);
+  if (max_num_tokens < num_tokens)
+    return fail(PSW_ERR_INVALID, "max_num_tokens (%d) < num_tokens (%d)", max_num_tokens,
+                num_tokens);
+  if (max_num_tokens > 0 && slot_mapping == nullptr)
+    return fail(PSW_ERR_INVALID, "slot_mapping is NULL");
+  if (num_tokens > 0 && (positions == nullptr || query_start_loc == nullptr ||
+                         (num_reqs > 0 && block_table == nullptr)))
+    return fail(PSW_ERR_INVALID, "query_start_loc, positions and block_table are required");
+  return check_hip(psw::launch_slot_mapping(query_start_loc, num_reqs, positions, num_tokens,
+                                            block_table, block_table_stride, block_size,
+                                            slot_mapping, max_num_tokens, (hipStream_t)stream),
+                   "slot_mapping");
+}
+
+int psw_kv_cache_write(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                       int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim_k,
+                       int32_t head_dim_v, void* k_cache, void* v_cache, int64_t num_slots,
+                       void* stream) {
+  if (num_tokens < 0 || num_kv_heads < 1 || num_slots < 0)
+    return fail(PSW_ERR_INVALID, "bad counts: num_tokens %d num_kv_heads %d num_slots %lld",
+                num_tokens, num_kv_heads, (long long)num_slots);
+  if (head_dim_k < 8 || head_dim_k % 8 != 0)
+    return fail(PSW_ERR_INVALID, "head_dim_k (%d) must be a positive multiple of 8", head_dim_k);
+  if ((v_new == nullptr) != (v_cache == nullptr))
+    return fail(PSW_ERR_INVALID, "v_new and v_cache must both be given or both be NULL");
+  if (v_new != nullptr && (head_dim_v < 8 || head_dim_v % 8 != 0))
+    return fail(PSW_ERR_INVALID, "head_dim_v (%d) must be a positive multiple of 8", head_dim_v);
+  if (num_tokens > 0 && (k_new == nullptr || slot_mapping == nullptr || k_cache == nullptr))
+    return fail(PSW_ERR_INVALID, "k_new, slot_mapping and k_cache are required");
+  return check_hip(psw::launch_kv_cache_write(
+                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                       slot_mapping, num_tokens, num_kv_heads, head_dim_k, head_dim_v,
+                       static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                       (hipStream_t)stream),
+                   "kv_cache_write");
+}
+
+static int fill_geometry(const psw_attn_args* a, psw::AttnParams& p, bool need_tensors) {
+  if (a == nullptr) return fail(PSW_ERR_INVALID, "args is NULL");
+  if (a->struct_size != (int32_t)sizeof(psw_attn_args))
+    return fail(PSW_ERR_INVALID, "struct_size %d != sizeof(psw_attn_args) %d", a->struct_size,
+                (int)sizeof(psw_attn_args));
+  if (a->num_seqs < 0 || a->num_tokens < 0 || a->num_q_heads < 1 || a->num_kv_heads < 1)
+    return fail(PSW_ERR_INVALID, "bad counts: seqs %d tokens %d q_heads %d kv_heads %d",
+                a->num_seqs, a->num_tokens, a->num_q_heads, a->num_kv_heads);
+  if (a->num_q_heads % a->num_kv_heads != 0)
+    return fail(PSW_ERR_INVALID, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                a->num_q_heads, a->num_kv_heads);
+  if (a->max_mm_ranges < 0 || (a->mm_ranges != nullptr && a->max_mm_ranges == 0))
+    return fail(PSW_ERR_INVALID, "max_mm_ranges %d inconsistent with mm_ranges", a->max_mm_ranges);
+  if (a->chunk_lookback >= 0 && a->chunk_size < 1)
+    return fail(PSW_ERR_INVALID, "chunk_size %d must be >= 1 with chunk_lookback %d",
+                a->chunk_size, a->chunk_lookback);
+  if (a->num_seqs > 0 && (a->query_start_loc == nullptr || a->seq_lens == nullptr))
+    return fail(PSW_ERR_INVALID, "query_start_loc and seq_lens are required");
+  if (need_tensors) {
+    if (a->head_dim_qk < 16 || a->head_dim_v < 16)
+      return fail(PSW_ERR_INVALID, "head dims %d/%d too small", a->head_dim_qk, a->head_dim_v);
+    if (!is_pow2(a->block_size))
+      return fail(PSW_ERR_INVALID, "block_size %d must be a power of two", a->block_size);
+    if (a->block_table_stride < 1)
+      return fail(PSW_ERR_INVALID, "block_table_stride %d must be >= 1", a->block_table_stride);
+    if (a->num_splits < 1 || (a->num_splits > 1 && a->key_ranges == nullptr))
+      return fail(PSW_ERR_INVALID, "num_splits %d needs key_ranges when > 1", a->num_splits);
+    if (a->out_dtype != PSW_BF16 && a->out_dtype != PSW_F32)
+      return fail(PSW_ERR_INVALID, "out_dtype %d unknown", a->out_dtype);
+    if (!(a->scale > 0.f) || !std::isfinite(a->scale))
+      return fail(PSW_ERR_INVALID, "scale must be finite and > 0");
+    if (a->num_tokens > 0 && (a->q == nullptr || a->k_cache == nullptr ||
+                              a->block_table == nullptr || a->out == nullptr))
+      return fail(PSW_ERR_INVALID, "q, k_cache, block_table and out are required");
+  }
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.k_cache = static_cast<const uint16_t*>(a->k_cache);
+  p.v_cache = a->v_cache ? static_cast<const uint16_t*>(a->v_cache) : p.k_cache;
+  p.block_table = a->block_table;
+  p.query_start_loc = a->query_start_loc;
+  p.seq_lens = a->seq_lens;
+  p.mm_ranges = a->max_mm_ranges > 0 ? a->mm_ranges : nullptr;
+  p.key_ranges = a->key_ranges;
+  p.out = a->out;
+  p.lse = a->lse;
+  p.num_seqs = a->num_seqs;
+  p.num_tokens = a->num_tokens;
+  p.num_q_heads = a->num_q_heads;
+  p.num_kv_heads = a->num_kv_heads;
+  p.queries_per_kv = a->num_q_heads / a->num_kv_heads;
+  p.head_dim_qk = a->head_dim_qk;
+  p.head_dim_v = a->head_dim_v;
+  p.block_size_log2 = is_pow2(a->block_size) ? log2i(a->block_size) : 0;
+  p.block_table_stride = a->block_table_stride;
+  p.max_mm_ranges = a->max_mm_ranges;
+  p.geom.window = a->window;
+  p.geom.causal = a->causal ? 1 : 0;
+  p.geom.chunk_size = a->chunk_size;
+  p.geom.chunk_lookback = a->chunk_lookback;
+  p.num_splits = a->num_splits;
+  p.out_f32 = a->out_dtype == PSW_F32;
+  p.scale_log2 = a->scale * psw::kLog2eHost;
+  return PSW_OK;
+}
+
+int psw_swa_mm_attention(const psw_attn_args* args, void* stream) {
+  psw::AttnParams p{};
+  int st = fill_geometry(args, p, true);
+  if (st != PSW_OK) return st;
+  const bool latent = args->v_cache == nullptr;
+  if (p.num_tokens == 0 || p.num_seqs == 0) return ok();
+  if (latent && psw::decode_supported(p))
+    return check_hip(psw::launch_attention_decode(p, (hipStream_t)stream), "attention(decode)");
+  if (psw::prefill_supported(p.head_dim_qk, p.head_dim_v, p.queries_per_kv, latent))
+    return check_hip(psw::launch_attention_prefill(p, (hipStream_t)stream), "attention(prefill)");
+  return fail(PSW_ERR_UNSUPPORTED,
+              "no kernel for head dims %d/%d, %d query heads per KV head, %s V",
+              p.head_dim_qk, p.head_dim_v, p.queries_per_kv, latent ? "latent" : "separate");
+}
+
+int psw_lse_combine(const void* const* partial_out, const float* const* partial_lse,
+                    int32_t num_partials, int32_t partial_dtype, int64_t num_rows,
+                    int32_t head_dim_v, void* out, int32_t out_dtype, float* out_lse,
+                    void* stream) {
+  if (num_partials < 1 || num_partials > psw::kMaxPartials)
+    return fail(PSW_ERR_INVALID, "num_partials %d outside [1, %d]", num_partials,
+                psw::kMaxPartials);
+  if (num_rows < 0) return fail(PSW_ERR_INVALID, "num_rows < 0");
+  if (head_dim_v < 8 || head_dim_v % 8 != 0 || head_dim_v > 1024)
+    return fail(PSW_ERR_INVALID, "head_dim_v %d must be a multiple of 8 in [8, 1024]", head_dim_v);
+  if ((partial_dtype != PSW_BF16 && partial_dtype != PSW_F32) ||
+      (out_dtype != PSW_BF16 && out_dtype != PSW_F32))
+    return fail(PSW_ERR_INVALID, "unknown dtype");
+  if (partial_out == nullptr || partial_lse == nullptr)
+    return fail(PSW_ERR_INVALID, "partial pointer arrays are required");
+  psw::CombineArgs parts{};
+  for (int i = 0; i < num_partials; ++i) {
+    if (num_rows > 0 && (partial_out[i] == nullptr || partial_lse[i] == nullptr))
+      return fail(PSW_ERR_INVALID, "partial %d is NULL", i);
+    parts.out[i] = partial_out[i];
+    parts.lse[i] = partial_lse[i];
+  }
+  if (num_rows > 0 && out == nullptr) return fail(PSW_ERR_INVALID, "out is NULL");
+  return check_hip(psw::launch_lse_combine(parts, num_partials, partial_dtype == PSW_F32,
+                                           num_rows, head_dim_v, out, out_dtype == PSW_F32,
+                                           out_lse, (hipStream_t)stream),
+                   "lse_combine");
+}
+
+int psw_tile_bounds(const psw_attn_args* geometry, int32_t tile_size, int32_t block_m,
+                    int32_t block_q, const int32_t* seq_idx, const int32_t* q_block_idx,
+                    int32_t num_queries, int32_t* out, void* stream) {
+  psw::AttnParams p{};
+  int st = fill_geometry(geometry, p, false);
+  if (st != PSW_OK) return st;
+  if (tile_size < 1 || block_m < 1 || block_q < 1 || num_queries < 0)
+    return fail(PSW_ERR_INVALID, "tile_size %d block_m %d block_q %d num_queries %d", tile_size,
+                block_m, block_q, num_queries);
+  if (num_queries > 0 && (seq_idx == nullptr || q_block_idx == nullptr || out == nullptr))
+    return fail(PSW_ERR_INVALID, "seq_idx, q_block_idx and out are required");
+  return check_hip(psw::launch_tile_bounds(p.query_start_loc, p.seq_lens, p.mm_ranges,
+                                           p.max_mm_ranges, p.queries_per_kv, p.geom, tile_size,
+                                           block_m, block_q, seq_idx, q_block_idx, num_queries,
+                                           out, (hipStream_t)stream),
+                   "tile_bounds");
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Device-side vocabulary shared by the gfx950 kernels: vector types, the two
+// bf16 MFMA shapes, the LDS transpose read, and small wave helpers.
+//
+// Lane layouts (checked on gfx950 with an in-bounds probe):
+//   v_mfma_f32_32x32x16_bf16  A[32][16]: lane l holds row l%32, k = (l/32)*8 .. +8
+//                             B[16][32]: lane l holds col l%32, k = (l/32)*8 .. +8
+//                             C[32][32]: lane l, reg i -> row (i/4)*8 + (l/32)*4 + i%4, col l%32
+//   ds_read_b64_tr_b16        inside each 16-lane group, result element j of lane i is
+//                             element i%4 of the 4 halfwords read by lane 4*j + i/4.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace psw {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Four bf16 read "transposed" out of LDS (see the layout note above).
+__device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) char*)(
+          (lds_void*)(p))));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Round eight fp32 to bf16 (nearest even) with v_cvt_pk_bf16_f32.
+__device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3, float a4,
+                                             float a5, float a6, float a7) {
+  bf16x2 p0 = __builtin_convertvector((f32x2){a0, a1}, bf16x2);
+  bf16x2 p1 = __builtin_convertvector((f32x2){a2, a3}, bf16x2);
+  bf16x2 p2 = __builtin_convertvector((f32x2){a4, a5}, bf16x2);
+  bf16x2 p3 = __builtin_convertvector((f32x2){a6, a7}, bf16x2);
+  bf16x4 q0 = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  bf16x4 q1 = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return cat8(q0, q1);
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(float a0, float a1, float a2, float a3) {
+  bf16x2 p0 = __builtin_convertvector((f32x2){a0, a1}, bf16x2);
+  bf16x2 p1 = __builtin_convertvector((f32x2){a2, a3}, bf16x2);
+  return __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float swap_halves(float x) {  // value of lane l ^ 32
+  return __shfl_xor(x, 32, kWave);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+}  // namespace psw

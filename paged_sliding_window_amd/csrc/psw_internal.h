@@ -1,0 +1,62 @@
+// Launchers behind the C ABI (implemented next to their kernels).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mask_bounds.h"
+
+namespace psw {
+
+// Everything the attention kernels read, already validated on the host.
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;  // == k_cache for the latent layout
+  const int32_t* block_table;
+  const int32_t* query_start_loc;
+  const int32_t* seq_lens;
+  const int32_t* mm_ranges;   // nullptr: no images
+  const int32_t* key_ranges;  // nullptr: one split over [0, seq_len)
+  void* out;
+  float* lse;
+  int num_seqs, num_tokens, num_q_heads, num_kv_heads, queries_per_kv;
+  int head_dim_qk, head_dim_v;
+  int block_size_log2, block_table_stride, max_mm_ranges;
+  MaskGeom geom;
+  int num_splits, out_f32;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+hipError_t launch_slot_mapping(const int32_t* qsl, int num_reqs, const int64_t* positions,
+                               int num_tokens, const int32_t* block_table, int stride,
+                               int block_size, int32_t* out, int max_num_tokens,
+                               hipStream_t stream);
+
+hipError_t launch_kv_cache_write(const uint16_t* k_new, const uint16_t* v_new,
+                                 const int32_t* slots, int num_tokens, int num_kv_heads,
+                                 int head_dim_k, int head_dim_v, uint16_t* k_cache,
+                                 uint16_t* v_cache, hipStream_t stream);
+
+constexpr int kMaxPartials = 64;
+struct CombineArgs {
+  const void* out[kMaxPartials];
+  const float* lse[kMaxPartials];
+};
+hipError_t launch_lse_combine(const CombineArgs& parts, int num_partials, int partial_f32,
+                              int64_t num_rows, int head_dim_v, void* out, int out_f32,
+                              float* out_lse, hipStream_t stream);
+
+hipError_t launch_tile_bounds(const int32_t* qsl, const int32_t* seq_lens,
+                              const int32_t* mm_ranges, int max_mm_ranges, int queries_per_kv,
+                              MaskGeom geom, int tile, int block_m, int block_q,
+                              const int32_t* seq_idx, const int32_t* q_block_idx, int n,
+                              int32_t* out, hipStream_t stream);
+
+// Returns hipErrorInvalidValue (not launched) when no kernel fits the shape.
+bool prefill_supported(int head_dim_qk, int head_dim_v, int queries_per_kv, bool latent);
+hipError_t launch_attention_prefill(const AttnParams& p, hipStream_t stream);
+
+bool decode_supported(const AttnParams& p);
+hipError_t launch_attention_decode(const AttnParams& p, hipStream_t stream);
+
+}  // namespace psw

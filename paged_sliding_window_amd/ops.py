@@ -1,0 +1,205 @@
+"""Torch-tensor wrappers with the C ABI's names (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import PSW_BF16, PSW_F32, PswAttnArgs, check, load
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: Optional[int] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def slot_mapping(query_start_loc: torch.Tensor, positions: torch.Tensor, block_table: torch.Tensor,
+                 block_size: int, max_num_tokens: int, out: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    _need(query_start_loc, "query_start_loc", torch.int32, 1)
+    _need(positions, "positions", torch.int64, 1)
+    _need(block_table, "block_table", torch.int32, 2)
+    if out is None:
+        out = torch.empty(max_num_tokens, dtype=torch.int32, device=positions.device)
+    _need(out, "out", torch.int32, 1)
+    if out.numel() < max_num_tokens:
+        raise ValueError("out is smaller than max_num_tokens")
+    check(load().psw_slot_mapping(_ptr(query_start_loc), query_start_loc.numel() - 1,
+                                  _ptr(positions), positions.numel(), _ptr(block_table),
+                                  block_table.shape[1], int(block_size), _ptr(out),
+                                  int(max_num_tokens), _stream(stream)))
+    return out
+
+
+def kv_cache_write(k_new: torch.Tensor, v_new: Optional[torch.Tensor], slots: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: Optional[torch.Tensor], stream=None) -> None:
+    """k_new [N, Hkv, Dk] bf16 -> k_cache [num_blocks, block_size, Hkv, Dk] (V likewise)."""
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    _need(slots, "slot_mapping", torch.int32, 1)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    n, hkv, dk = k_new.shape
+    dv = 0
+    if v_new is not None:
+        _need(v_new, "v_new", torch.bfloat16, 3)
+        _need(v_cache, "v_cache", torch.bfloat16, 4)
+        dv = v_new.shape[2]
+    if slots.numel() < n:
+        raise ValueError("slot_mapping shorter than the new rows")
+    num_slots = k_cache.shape[0] * k_cache.shape[1]
+    check(load().psw_kv_cache_write(_ptr(k_new), _ptr(v_new), _ptr(slots), n, hkv, dk, dv,
+                                    _ptr(k_cache), _ptr(v_cache), num_slots, _stream(stream)))
+
+
+def _attn_args(q, k_cache, v_cache, block_table, query_start_loc, seq_lens, *, scale, window,
+               causal, chunk_size, chunk_lookback, mm_ranges, key_ranges, out, lse, head_dim_v,
+               out_dtype, num_splits) -> PswAttnArgs:
+    a = PswAttnArgs()
+    a.struct_size = ctypes.sizeof(PswAttnArgs)
+    a.q, a.k_cache, a.v_cache = _ptr(q), _ptr(k_cache), _ptr(v_cache)
+    a.block_table, a.query_start_loc, a.seq_lens = _ptr(block_table), _ptr(query_start_loc), _ptr(seq_lens)
+    a.mm_ranges, a.key_ranges = _ptr(mm_ranges), _ptr(key_ranges)
+    a.out, a.lse = _ptr(out), _ptr(lse)
+    a.num_seqs = query_start_loc.numel() - 1
+    a.num_tokens = q.shape[0] if q is not None else 0
+    a.num_q_heads = q.shape[1] if q is not None else 1
+    a.num_kv_heads = k_cache.shape[2] if k_cache is not None else 1
+    a.head_dim_qk = q.shape[2] if q is not None else 0
+    a.head_dim_v = head_dim_v
+    a.block_size = k_cache.shape[1] if k_cache is not None else 1
+    a.block_table_stride = block_table.shape[1] if block_table is not None else 1
+    a.max_mm_ranges = mm_ranges.shape[1] if mm_ranges is not None else 0
+    a.window, a.causal = int(window), int(bool(causal))
+    a.chunk_size, a.chunk_lookback = int(chunk_size), int(chunk_lookback)
+    a.num_splits = int(num_splits)
+    a.out_dtype = out_dtype
+    a.scale = float(scale)
+    return a
+
+
+def swa_mm_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor],
+                     block_table: torch.Tensor, query_start_loc: torch.Tensor,
+                     seq_lens: torch.Tensor, *, scale: float, window: int, causal: bool,
+                     chunk_size: int = 0, chunk_lookback: int = -1,
+                     mm_ranges: Optional[torch.Tensor] = None,
+                     key_ranges: Optional[torch.Tensor] = None, head_dim_v: Optional[int] = None,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     out_dtype: torch.dtype = torch.bfloat16, return_lse: bool = False,
+                     stream=None):
+    """Paged attention; with key_ranges [S, num_seqs, 2] it writes S fp32/bf16
+    partials out[S, N, Hq, Dv] and lse[S, N, Hq]."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    if v_cache is not None:
+        _need(v_cache, "v_cache", torch.bfloat16, 4)
+        head_dim_v = v_cache.shape[3]
+    elif head_dim_v is None:
+        raise ValueError("head_dim_v is required for a latent cache (v_cache=None)")
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(query_start_loc, "query_start_loc", torch.int32, 1)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    if mm_ranges is not None:
+        _need(mm_ranges, "mm_ranges", torch.int32, 3)
+    num_splits = 1
+    if key_ranges is not None:
+        _need(key_ranges, "key_ranges", torch.int32, 3)
+        num_splits = key_ranges.shape[0]
+    n, hq = q.shape[0], q.shape[1]
+    odt = {torch.bfloat16: PSW_BF16, torch.float32: PSW_F32}[out_dtype]
+    if out is None:
+        out = torch.empty((num_splits, n, hq, head_dim_v), dtype=out_dtype, device=q.device)
+    _need(out, "out", out_dtype)
+    if out.numel() != num_splits * n * hq * head_dim_v:
+        raise ValueError("out has the wrong size")
+    if lse is None and (return_lse or num_splits > 1):
+        lse = torch.empty((num_splits, n, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+        if lse.numel() != num_splits * n * hq:
+            raise ValueError("lse has the wrong size")
+    a = _attn_args(q, k_cache, v_cache, block_table, query_start_loc, seq_lens, scale=scale,
+                   window=window, causal=causal, chunk_size=chunk_size,
+                   chunk_lookback=chunk_lookback, mm_ranges=mm_ranges, key_ranges=key_ranges,
+                   out=out, lse=lse, head_dim_v=head_dim_v, out_dtype=odt,
+                   num_splits=num_splits)
+    check(load().psw_swa_mm_attention(ctypes.byref(a), _stream(stream)))
+    if key_ranges is None:
+        out = out.view(n, hq, head_dim_v)
+        if lse is not None:
+            lse = lse.view(n, hq)
+    return (out, lse) if (return_lse or num_splits > 1) else out
+
+
+def lse_combine(partial_outs: Sequence[torch.Tensor], partial_lses: Sequence[torch.Tensor],
+                out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
+                out_dtype: torch.dtype = torch.bfloat16, stream=None):
+    """Merge P partials [rows, Dv] (fp32 or bf16) with lse [rows] fp32 in place."""
+    P = len(partial_outs)
+    if P != len(partial_lses) or P == 0:
+        raise ValueError("need as many LSE tensors as partial outputs, at least one")
+    pdt = partial_outs[0].dtype
+    for i, (o, l) in enumerate(zip(partial_outs, partial_lses)):
+        _need(o, f"partial_outs[{i}]", pdt)
+        _need(l, f"partial_lses[{i}]", torch.float32)
+    dv = partial_outs[0].shape[-1]
+    rows = partial_outs[0].numel() // dv
+    for o, l in zip(partial_outs, partial_lses):
+        if o.numel() != rows * dv or l.numel() != rows:
+            raise ValueError("partials disagree in size")
+    if out is None:
+        out = torch.empty((rows, dv), dtype=out_dtype, device=partial_outs[0].device)
+    _need(out, "out", out_dtype)
+    if out_lse is not None:
+        _need(out_lse, "out_lse", torch.float32)
+    po = (ctypes.c_void_p * P)(*[o.data_ptr() for o in partial_outs])
+    pl = (ctypes.c_void_p * P)(*[l.data_ptr() for l in partial_lses])
+    check(load().psw_lse_combine(po, pl, P, {torch.bfloat16: PSW_BF16, torch.float32: PSW_F32}[pdt],
+                                 rows, dv, _ptr(out),
+                                 {torch.bfloat16: PSW_BF16, torch.float32: PSW_F32}[out_dtype],
+                                 _ptr(out_lse), _stream(stream)))
+    return out if out_lse is None else (out, out_lse)
+
+
+def tile_bounds(query_start_loc: torch.Tensor, seq_lens: torch.Tensor,
+                mm_ranges: Optional[torch.Tensor], *, num_q_heads: int, num_kv_heads: int,
+                window: int, causal: bool, chunk_size: int, chunk_lookback: int, tile_size: int,
+                block_m: int, block_q: int, seq_idx: torch.Tensor, q_block_idx: torch.Tensor,
+                stream=None) -> torch.Tensor:
+    """(loop_lo, loop_hi, max_seq_prefix_len) per (seq_idx[n], q_block_idx[n])."""
+    _need(query_start_loc, "query_start_loc", torch.int32, 1)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(seq_idx, "seq_idx", torch.int32, 1)
+    _need(q_block_idx, "q_block_idx", torch.int32, 1)
+    if mm_ranges is not None:
+        _need(mm_ranges, "mm_ranges", torch.int32, 3)
+    a = PswAttnArgs()
+    a.struct_size = ctypes.sizeof(PswAttnArgs)
+    a.query_start_loc, a.seq_lens, a.mm_ranges = _ptr(query_start_loc), _ptr(seq_lens), _ptr(mm_ranges)
+    a.num_seqs = query_start_loc.numel() - 1
+    a.num_q_heads, a.num_kv_heads = int(num_q_heads), int(num_kv_heads)
+    a.max_mm_ranges = mm_ranges.shape[1] if mm_ranges is not None else 0
+    a.window, a.causal = int(window), int(bool(causal))
+    a.chunk_size, a.chunk_lookback = int(chunk_size), int(chunk_lookback)
+    n = seq_idx.numel()
+    out = torch.empty((n, 3), dtype=torch.int32, device=seq_idx.device)
+    check(load().psw_tile_bounds(ctypes.byref(a), int(tile_size), int(block_m), int(block_q),
+                                 _ptr(seq_idx), _ptr(q_block_idx), n, _ptr(out), _stream(stream)))
+    return out

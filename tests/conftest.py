@@ -16,3 +16,13 @@ def pytest_configure(config):
 def pytest_collection_modifyitems(config, items):
     # GPU tests run in file order after the CPU ones; nothing to reorder.
     return
+
+
+@pytest.fixture(autouse=True)
+def _gpu_guard(request):
+    """GPU tests need a visible GPU; on a GPU machine a missing library still fails loudly."""
+    if request.node.get_closest_marker("gpu") is not None:
+        import torch
+        if not torch.cuda.is_available():
+            pytest.skip("no GPU visible")
+        print(f"\n[gpu-test] {request.node.nodeid}", flush=True)

@@ -1,0 +1,81 @@
+"""C-ABI checks that need no GPU: the library is built, loads, exports every
+function include/psw.h declares, and rejects bad arguments on the host before
+touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_sliding_window_amd as psw
+from paged_sliding_window_amd._lib import (EXPORTS, PSW_ERR_INVALID, PSW_OK, PswAttnArgs)
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "psw.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(psw_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = psw.load()
+    names = declared_functions()
+    assert names, "no declarations found"
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in EXPORTS, f"{n} has no ctypes declaration"
+    assert sorted(EXPORTS) == names
+
+
+def test_version_and_status_strings():
+    lib = psw.load()
+    assert lib.psw_abi_version() == 1
+    assert lib.psw_status_string(PSW_OK) == b"ok"
+    assert lib.psw_status_string(PSW_ERR_INVALID) == b"invalid argument"
+
+
+def _args(**kw):
+    a = PswAttnArgs()
+    a.struct_size = ctypes.sizeof(PswAttnArgs)
+    a.num_seqs, a.num_tokens, a.num_q_heads, a.num_kv_heads = 0, 0, 8, 2
+    a.head_dim_qk = a.head_dim_v = 128
+    a.block_size, a.block_table_stride, a.num_splits, a.scale = 16, 1, 1, 0.1
+    a.chunk_lookback = -1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_struct_size_matches_the_c_struct():
+    lib = psw.load()
+    assert lib.psw_swa_mm_attention(ctypes.byref(_args()), None) == PSW_OK   # nothing to launch
+    bad = _args(struct_size=ctypes.sizeof(PswAttnArgs) - 4)
+    assert lib.psw_swa_mm_attention(ctypes.byref(bad), None) == PSW_ERR_INVALID
+    assert b"struct_size" in lib.psw_last_error()
+
+
+@pytest.mark.parametrize("field,value", [
+    ("num_q_heads", 7), ("block_size", 12), ("scale", 0.0), ("num_splits", 2),
+    ("out_dtype", 9), ("num_tokens", -1), ("chunk_size", 0),
+])
+def test_attention_rejects_bad_scalars(field, value):
+    kw = {field: value}
+    if field == "chunk_size":
+        kw["chunk_lookback"] = 1
+    lib = psw.load()
+    assert lib.psw_swa_mm_attention(ctypes.byref(_args(**kw)), None) == PSW_ERR_INVALID
+
+
+def test_other_entry_points_reject_bad_scalars():
+    lib = psw.load()
+    assert lib.psw_slot_mapping(None, -1, None, 0, None, 1, 16, None, 0, None) == PSW_ERR_INVALID
+    assert lib.psw_slot_mapping(None, 0, None, 5, None, 1, 16, None, 4, None) == PSW_ERR_INVALID
+    assert lib.psw_slot_mapping(None, 0, None, 0, None, 1, 16, None, 0, None) == PSW_OK
+    assert lib.psw_kv_cache_write(None, None, None, 0, 1, 12, 0, None, None, 0, None) == PSW_ERR_INVALID
+    po = (ctypes.c_void_p * 1)()
+    assert lib.psw_lse_combine(po, po, 0, 0, 1, 64, None, 0, None, None) == PSW_ERR_INVALID
+    assert lib.psw_lse_combine(po, po, 65, 0, 1, 64, None, 0, None, None) == PSW_ERR_INVALID
+    assert lib.psw_lse_combine(po, po, 1, 0, 1, 12, None, 0, None, None) == PSW_ERR_INVALID
+    assert lib.psw_tile_bounds(ctypes.byref(_args()), 0, 16, 8, None, None, 0, None, None) == PSW_ERR_INVALID

@@ -1,0 +1,115 @@
+"""GPU parity: paged prefill attention against the float64 oracle, element by
+element within |g - r| <= 2e-2 + 2e-2 |r| (bf16 inputs, fp32 accumulation)."""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_setup import GpuWorkload, assert_close, assert_lse_close, oracle_rows
+from workloads import make_config, make_small_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(gw, out, lse, rows_per_seq=None, seed=0):
+    w = gw.w
+    out = out.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    rng = np.random.default_rng(seed)
+    for r in range(w.num_seqs):
+        ql = int(w.query_lens[r])
+        rows = None
+        if rows_per_seq is not None and ql > rows_per_seq:
+            rows = np.unique(np.concatenate([np.arange(8), ql - 1 - np.arange(8),
+                                             rng.choice(ql, rows_per_seq, replace=False)]))
+        ref_o, ref_l = oracle_rows(w, r, rows)
+        s0 = int(w.query_start_loc[r])
+        sel = np.arange(ql) if rows is None else rows
+        assert_close(out[s0 + sel], ref_o, f"{w.name} seq {r} out")
+        assert_lse_close(lse[s0 + sel], ref_l, f"{w.name} seq {r} lse")
+
+
+def test_tiny_prefill_full_and_image_sensitivity():
+    w = make_config(1)
+    gw = GpuWorkload(w)
+    out, lse = gw.attention()
+    _check(gw, out, lse)
+    # the image range matters: the no-image oracle must fail the same tolerance
+    ref_no_mm, _ = oracle_rows(w, 0, ranges=False)
+    got = out.float().cpu().numpy()
+    err = np.abs(got - ref_no_mm)
+    assert (err > 2e-2 + 2e-2 * np.abs(ref_no_mm)).any()
+    out_no_mm, _ = gw.attention(mm=False)
+    assert_close(out_no_mm.float().cpu().numpy(), ref_no_mm, "no-image run")
+
+
+def test_batched_chunked_prefill_full():
+    gw = GpuWorkload(make_config(3))
+    out, lse = gw.attention()
+    _check(gw, out, lse)
+
+
+def test_noncausal_chunk_lookback_sampled():
+    gw = GpuWorkload(make_config(4))
+    out, lse = gw.attention()
+    _check(gw, out, lse, rows_per_seq=600, seed=4)
+
+
+def test_gemma_multimodal_prefill_full_size_sampled():
+    w = make_config(2)
+    gw = GpuWorkload(w)
+    out, lse = gw.attention()
+    # rows around every image boundary plus random rows
+    rows = set(np.random.default_rng(2).choice(16550, 200, replace=False).tolist())
+    for s, e in w.ranges_of(0)[::6]:
+        rows.update([s - 1, s, s + 1, e - 1, e, e + 1])
+    rows = np.array(sorted(x for x in rows if 0 <= x < 16550))
+    ref_o, ref_l = oracle_rows(w, 0, rows)
+    assert_close(out.float().cpu().numpy()[rows], ref_o, "gemma out")
+    assert_lse_close(lse.cpu().numpy()[rows], ref_l, "gemma lse")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_small_cases(seed):
+    rng = np.random.default_rng(seed)
+    d = int(rng.choice([64, 128, 256]))
+    hkv = int(rng.choice([1, 2]))
+    qpk = int(rng.choice([1, 2, 3, 8]))
+    w = make_small_case(500 + seed, num_seqs=int(rng.integers(1, 5)), max_len=700, hq=hkv * qpk,
+                        hkv=hkv, d=d, block_size=int(rng.choice([1, 16, 64])))
+    gw = GpuWorkload(w)
+    out, lse = gw.attention()
+    _check(gw, out, lse)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_key_split_partials_and_fp32_output(seed):
+    w = make_small_case(700 + seed, num_seqs=3, max_len=500, hq=4, hkv=2, d=128)
+    gw = GpuWorkload(w)
+    rng = np.random.default_rng(seed)
+    S = 3
+    kr = np.zeros((S, w.num_seqs, 2), dtype=np.int32)
+    for r in range(w.num_seqs):
+        L = int(w.seq_lens[r])
+        cuts = np.sort(rng.integers(0, L + 1, size=S - 1))
+        edges = np.concatenate([[0], cuts, [L]])
+        kr[:, r, 0], kr[:, r, 1] = edges[:-1], edges[1:]
+    out, lse = gw.attention(key_ranges=kr, out_dtype=torch.float32)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for j in range(S):
+        for r in range(w.num_seqs):
+            s0, s1 = int(w.query_start_loc[r]), int(w.query_start_loc[r + 1])
+            ref_o, ref_l = oracle_rows(w, r, key_range=tuple(kr[j, r]))
+            assert_close(out[j, s0:s1], ref_o, f"split {j} seq {r}")
+            assert_lse_close(lse[j, s0:s1], ref_l, f"split {j} seq {r} lse")
+
+
+def test_empty_batch_is_a_no_op():
+    w = make_small_case(1, num_seqs=1, max_len=40)
+    gw = GpuWorkload(w)
+    import paged_sliding_window_amd as psw
+    q0 = gw.q[:0]
+    qsl = torch.zeros(2, dtype=torch.int32, device="cuda")
+    out = psw.swa_mm_attention(q0, gw.k_cache, gw.v_cache, gw.block_table, qsl, gw.seq_lens,
+                               scale=1.0, window=0, causal=True)
+    torch.cuda.synchronize()
+    assert out.numel() == 0

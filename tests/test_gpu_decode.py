@@ -1,0 +1,93 @@
+"""GPU parity: latent (MLA-shaped) split-KV decode, history partials + current
+partial merged by the LSE combine, against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import paged_sliding_window_amd as psw
+from oracle import lse_merge_ref
+from tests.gpu_setup import (GpuWorkload, assert_close, assert_lse_close, i32, oracle_rows)
+from workloads import make_config, make_small_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode(gw, w, partial_dtype=torch.float32):
+    hist_o, hist_l = gw.attention(key_ranges=w.key_ranges, out_dtype=partial_dtype)
+    cur_o, cur_l = gw.attention(key_ranges=w.current_ranges, out_dtype=partial_dtype)
+    S = hist_o.shape[0]
+    rows = w.num_tokens * w.num_q_heads
+    outs = [hist_o[j].view(rows, w.head_dim_v) for j in range(S)] + [cur_o[0].view(rows, w.head_dim_v)]
+    lses = [hist_l[j].view(rows) for j in range(S)] + [cur_l[0].view(rows)]
+    lse_out = torch.empty(rows, dtype=torch.float32, device="cuda")
+    out = psw.lse_combine(outs, lses, out_lse=lse_out)[0]
+    return out, lse_out, hist_o, hist_l, cur_o, cur_l
+
+
+def test_mla_decode_full_size():
+    w = make_config(5)
+    gw = GpuWorkload(w)
+    out, lse, hist_o, hist_l, cur_o, cur_l = _decode(gw, w)
+    out = out.float().cpu().numpy().reshape(w.num_tokens, w.num_q_heads, w.head_dim_v)
+    lse = lse.cpu().numpy().reshape(w.num_tokens, w.num_q_heads)
+    for r in range(w.num_seqs):
+        ref_o, ref_l = oracle_rows(w, r)
+        assert_close(out[r], ref_o[0], f"token {r}")
+        assert_lse_close(lse[r], ref_l[0], f"token {r} lse")
+    # the partials themselves, on a few requests
+    ho, hl = hist_o.cpu().numpy(), hist_l.cpu().numpy()
+    for r in (0, 17, 63):
+        for j in range(w.key_ranges.shape[0]):
+            ref_o, ref_l = oracle_rows(w, r, key_range=tuple(w.key_ranges[j, r]))
+            assert_close(ho[j, r], ref_o[0], f"history split {j} of {r}")
+            assert_lse_close(hl[j, r], ref_l[0], f"history split {j} of {r} lse")
+        ref_o, ref_l = oracle_rows(w, r, key_range=tuple(w.current_ranges[0, r]))
+        assert_close(cur_o[0, r].cpu().numpy(), ref_o[0], f"current of {r}")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_small_latent_decode_bf16_partials(seed):
+    from workloads.synth import decode_split_ranges
+    w = make_small_case(900 + seed, num_seqs=5, max_len=3000, hq=64, hkv=1, d=576, dv=512,
+                        window=0, causal=True, chunk=(0, -1), max_ranges=0, latent=True,
+                        block_size=64)
+    # one new token per request: keep only the last position of each request
+    qsl = np.arange(w.num_seqs + 1, dtype=np.int32)
+    last = w.query_start_loc[1:] - 1
+    w.q_bits = w.q_bits[last]
+    w.positions = (w.seq_lens - 1).astype(np.int64)
+    w.context_lens = w.seq_lens - 1
+    w.query_lens = np.ones(w.num_seqs, dtype=np.int64)
+    w.query_start_loc = qsl
+    w.key_ranges = decode_split_ranges(w.seq_lens, 4)
+    w.current_ranges = np.stack([np.stack([w.seq_lens - 1, w.seq_lens], 1)]).astype(np.int32)
+    gw = GpuWorkload(w)
+    out, lse, *_ = _decode(gw, w, partial_dtype=torch.bfloat16)
+    out = out.float().cpu().numpy().reshape(w.num_tokens, w.num_q_heads, w.head_dim_v)
+    for r in range(w.num_seqs):
+        ref_o, _ = oracle_rows(w, r)
+        assert_close(out[r], ref_o[0], f"token {r}")
+
+
+@pytest.mark.parametrize("P,pdt,odt", [(1, torch.float32, torch.bfloat16),
+                                        (9, torch.float32, torch.bfloat16),
+                                        (9, torch.bfloat16, torch.float32),
+                                        (64, torch.float32, torch.float32)])
+def test_lse_combine_random_partials(P, pdt, odt):
+    rng = np.random.default_rng(P)
+    rows, dv = 777, 512 if P < 64 else 64
+    outs = [rng.standard_normal((rows, dv)).astype(np.float32) for _ in range(P)]
+    lses = [rng.normal(0, 4, rows).astype(np.float32) for _ in range(P)]
+    for l in lses:
+        l[rng.random(rows) < 0.3] = -np.inf
+    lses[0][:5] = -np.inf
+    for l in lses:
+        l[:5] = -np.inf            # rows with every partial empty
+    t_outs = [torch.from_numpy(o).cuda().to(pdt) for o in outs]
+    ref_in = [t.float().cpu().numpy() for t in t_outs]   # what the kernel actually reads
+    t_lses = [torch.from_numpy(l).cuda() for l in lses]
+    out_lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+    out, ol = psw.lse_combine(t_outs, t_lses, out_lse=out_lse, out_dtype=odt)
+    ref_o, ref_l = lse_merge_ref(ref_in, lses)
+    assert_close(out.float().cpu().numpy(), ref_o, "combine out")
+    assert_lse_close(ol.cpu().numpy(), ref_l, "combine lse")
