@@ -1,0 +1,300 @@
+"""Benchmark of the paged sliding-window + clamped image-range hot path on one GPU.
+
+One step = the whole path over one synthetic batch of the Gemma-style
+multimodal prefill (16,550 tokens, 60 images of 256 tokens, W 1024, 16 query /
+8 KV heads, head dim 256, paged in blocks of 16):
+  slot mapping of the new tokens -> KV-cache write -> paged prefill attention.
+The decode half of the path (MLA-shaped split-KV decode: 64 requests, 128 heads,
+576/512 latent, 8 history splits + the current key, LSE combine) is timed in
+the same run and reported under "decode".
+
+Reported value: algorithmic TFLOP/s = 4 * head_dim FLOP per allowed
+(query, key, head) triple, 3.0115e11 per step, over the measured step time.
+The "roofline" object is for the dominant kernel (prefill attention), timed
+with HIP events around each of its launches on the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
+    ap.add_argument("--skip-decode", action="store_true", help="omit the decode half")
+    ap.add_argument("--decode-splits", type=int, default=8)
+    return ap.parse_args()
+
+
+def allowed_pairs_per_head(w, r):
+    """Allowed (query, key) pairs of request r for one head: each causal row's
+    allowed keys form one interval (window part and image part both contain the
+    query position), so the count is the interval length."""
+    total = 0
+    ctx = int(w.context_lens[r])
+    L = int(w.seq_lens[r])
+    ranges = [(s, e) for s, e in w.ranges_of(r) if s < e]
+    W = w.window
+    for i in range(int(w.query_lens[r])):
+        q = ctx + i
+        lo = max(0, q - W + 1) if W > 0 else 0
+        hi = q
+        for s, e in ranges:
+            if s <= q <= e:
+                lo = min(lo, max(s, q - W + 1) if W > 0 else s)
+                hi = max(hi, e)
+        total += min(hi, L - 1) - lo + 1
+    return total
+
+
+def prefill_flop(w):
+    pairs = sum(allowed_pairs_per_head(w, r) for r in range(w.num_seqs))
+    return pairs * w.num_q_heads * 4 * w.head_dim_qk, pairs
+
+
+def cpu_baseline(w, pairs_per_head_fn):
+    """The oracle (as written) on a bounded sample of the prefill workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention_ref
+    r = 0
+    rows = np.arange(8000, 8000 + 1536)
+    q = w.q_f32()
+    k, v = w.k_f32(r), w.v_f32(r)
+    t0 = time.perf_counter()
+    attention_ref(q, k, v, context_len=0, seq_len=int(w.seq_lens[r]), scale=w.scale,
+                  window=w.window, causal=w.causal, ranges=w.ranges_of(r), rows=rows)
+    dt = time.perf_counter() - t0
+    pairs = 0
+    W = w.window
+    ranges = w.ranges_of(r)
+    for qq in rows:
+        lo, hi = max(0, qq - W + 1), qq
+        for s, e in ranges:
+            if s < e and s <= qq <= e:
+                lo, hi = min(lo, max(s, qq - W + 1)), max(hi, e)
+        pairs += hi - lo + 1
+    flop = pairs * w.num_q_heads * 4 * w.head_dim_qk
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle, rows {rows[0]}..{rows[-1]} (1536 of 16550) of the "
+                      f"Gemma-style prefill, all 16 heads; {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path's multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import paged_sliding_window_amd as psw
+    from tests.gpu_setup import GpuWorkload, bits_to_bf16, i32, i64
+    from workloads import make_config
+
+    torch.cuda.set_device(0)
+    psw.load()
+    t_setup = time.perf_counter()
+
+    # ---------------- prefill (headline) ----------------
+    log("generating the prefill workload")
+    w = make_config(2)
+    flop, pairs = prefill_flop(w)
+    gw = GpuWorkload(w, fill_cache=False)
+    # the context part is empty (context_len 0): the step writes every new K/V row
+    k_new = bits_to_bf16(np.concatenate(w.k_bits))
+    v_new = bits_to_bf16(np.concatenate(w.v_bits))
+    slots = torch.empty(w.max_num_tokens, dtype=torch.int32, device="cuda")
+    out = torch.empty((w.num_tokens, w.num_q_heads, w.head_dim_v), dtype=torch.bfloat16,
+                      device="cuda")
+    lse = torch.empty((w.num_tokens, w.num_q_heads), dtype=torch.float32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def prefill_step(i=None):
+        psw.slot_mapping(gw.qsl, gw.positions, gw.block_table, w.block_size, w.max_num_tokens,
+                         out=slots)
+        psw.kv_cache_write(k_new, v_new, slots, gw.k_cache, gw.v_cache)
+        if i is not None:
+            ev[i][0].record()
+        psw.swa_mm_attention(gw.q, gw.k_cache, gw.v_cache, gw.block_table, gw.qsl, gw.seq_lens,
+                             scale=w.scale, window=w.window, causal=w.causal,
+                             mm_ranges=gw.mm_ranges, out=out, lse=lse)
+        if i is not None:
+            ev[i][1].record()
+
+    log("timing prefill")
+    for _ in range(args.warmup):
+        prefill_step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        prefill_step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / args.steps
+    attn_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (attn_ms * 1e-3) / 1e12
+
+    result = {
+        "metric": "SWA+MM-prefix prefill attn TFLOP/s (% MFMA peak); paged decode HBM GB/s",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "gemma_mm_prefill_16550",
+            "tokens": w.num_tokens, "window": w.window, "causal": True, "images": 60,
+            "image_tokens": 256, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim_qk, "block_size": w.block_size,
+            "allowed_pairs_per_head": pairs, "flop_per_step": flop,
+            "step": "slot_mapping + kv_cache_write + swa_mm_attention",
+        },
+        "roofline": {
+            "kernel": "prefill_attention_kernel<256,256>",
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_ms": round(attn_ms, 5),
+        },
+    }
+    del gw, k_new, v_new, out, lse
+    torch.cuda.empty_cache()
+
+    # ---------------- decode (second half of the path) ----------------
+    log(f"prefill {ms_per_step:.4f} ms/step, attention {attn_ms:.4f} ms")
+    if not args.skip_decode:
+        log("decode half")
+        result["decode"] = bench_decode(args, torch, psw, np)
+
+    if not args.skip_cpu:
+        log("CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(w, allowed_pairs_per_head)
+    result["setup_s"] = round(time.perf_counter() - t_setup, 1)
+    print(json.dumps(result), flush=True)
+
+
+def bench_decode(args, torch, psw, np):
+    from tests.gpu_setup import bits_to_bf16, i32, i64
+    from workloads import make_config
+    from workloads.synth import decode_split_ranges
+
+    w = make_config(5, decode_splits=args.decode_splits)
+    log("decode workload generated")
+    B = w.block_size
+    R, H, DV = w.num_seqs, w.num_q_heads, w.head_dim_v
+    q = bits_to_bf16(w.q_bits)
+    bt = i32(w.block_table)
+    qsl = i32(w.query_start_loc)
+    seq_lens = i32(w.seq_lens)
+    positions = i64(w.positions)
+    cache = torch.empty((w.num_blocks, B, 1, w.head_dim_qk), dtype=torch.bfloat16, device="cuda")
+    # context rows [0, L-1) go in before timing, through the library itself
+    qsl_ctx = np.concatenate([[0], np.cumsum(w.seq_lens - 1)]).astype(np.int32)
+    pos_ctx = np.concatenate([np.arange(int(L) - 1) for L in w.seq_lens]).astype(np.int64)
+    slots_ctx = psw.slot_mapping(i32(qsl_ctx), i64(pos_ctx), bt, B, int(qsl_ctx[-1]))
+    psw.kv_cache_write(bits_to_bf16(np.concatenate([k[:-1] for k in w.k_bits])), None, slots_ctx,
+                       cache, None)
+    new_rows = bits_to_bf16(np.stack([k[-1] for k in w.k_bits]))
+    del slots_ctx
+    kr_hist = i32(w.key_ranges)
+    kr_cur = i32(w.current_ranges)
+    S = w.key_ranges.shape[0]
+    hist_o = torch.empty((S, R, H, DV), dtype=torch.float32, device="cuda")
+    hist_l = torch.empty((S, R, H), dtype=torch.float32, device="cuda")
+    cur_o = torch.empty((1, R, H, DV), dtype=torch.float32, device="cuda")
+    cur_l = torch.empty((1, R, H), dtype=torch.float32, device="cuda")
+    out = torch.empty((R * H, DV), dtype=torch.bfloat16, device="cuda")
+    slots = torch.empty(R, dtype=torch.int32, device="cuda")
+    outs = [hist_o[j].view(R * H, DV) for j in range(S)] + [cur_o[0].view(R * H, DV)]
+    lses = [hist_l[j].view(R * H) for j in range(S)] + [cur_l[0].view(R * H)]
+    steps = max(args.steps, 10)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+
+    def step(i=None):
+        psw.slot_mapping(qsl, positions, bt, B, R, out=slots)
+        psw.kv_cache_write(new_rows, None, slots, cache, None)
+        if i is not None:
+            ev[i][0].record()
+        psw.swa_mm_attention(q, cache, None, bt, qsl, seq_lens, scale=w.scale, window=0,
+                             causal=True, key_ranges=kr_hist, head_dim_v=DV, out=hist_o,
+                             lse=hist_l, out_dtype=torch.float32)
+        psw.swa_mm_attention(q, cache, None, bt, qsl, seq_lens, scale=w.scale, window=0,
+                             causal=True, key_ranges=kr_cur, head_dim_v=DV, out=cur_o,
+                             lse=cur_l, out_dtype=torch.float32)
+        if i is not None:
+            ev[i][1].record()
+        psw.lse_combine(outs, lses, out=out)
+        if i is not None:
+            ev[i][2].record()
+
+    log("timing decode")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    comb_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    kv_bytes = int(w.seq_lens.sum()) * w.head_dim_qk * 2
+    alg_bytes = (kv_bytes + q.numel() * 2 + w.block_table.size * 4 + out.numel() * 2)
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    attn_gbs = (kv_bytes + q.numel() * 2) / (attn_ms * 1e-3) / 1e9
+    return {
+        "workload": "mla_splitkv_decode_b64",
+        "unit": "GB/s",
+        "value": round(gbs, 1),
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "ms_per_step": round(ms, 5),
+        "algorithmic_bytes_per_step": alg_bytes,
+        "attention_ms": round(attn_ms, 5),
+        "attention_GBps": round(attn_gbs, 1),
+        "combine_ms": round(comb_ms, 5),
+        "history_splits": S,
+        "step": "slot_mapping + kv_cache_write + history and current partials + lse_combine",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -3,48 +3,80 @@
 // (vLLM PR #53147 summary, "Implementation breakdown" and "Key source snippet").
 //
 // Work decomposition (gfx950, wave64):
-//   * one workgroup = one query block x one KV head x one key split; 4 waves,
-//     32 rows each, 128 rows = (128 / queries_per_kv) positions x the query heads
-//     of that KV head (rows position-major), so a K/V tile staged in LDS serves
-//     every query head sharing it;
-//   * KV tiles of 64 keys, gathered from the paged cache through the block table
-//     with 16-byte loads (each key's row is contiguous) and staged in LDS in the
-//     cache's own [key][dim] layout;
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K from LDS as the A operand,
-//     Q held in registers as the B operand, so each lane ends up holding 32
-//     scores of ONE query row (the other 32 keys of the row sit in lane ^ 32);
-//     the online softmax then needs a single cross-half exchange per tile;
-//   * O^T += V^T P^T: P^T comes straight from the S^T accumulators (converted
-//     to bf16), V^T is read out of the row-major V tile with ds_read_b64_tr_b16,
-//     and O^T keeps one query row per lane, so the rescale is per lane;
-//   * per-element masking only on tiles that are not entirely inside every
-//     row's allowed interval (each row's allowed keys form one interval).
+//   * one workgroup = one query block x one KV head x one key split; WAVES waves
+//     of 32 rows each.  Rows are (position, query head of this KV head) in
+//     position-major order, so one K/V tile in LDS serves every query head that
+//     shares it (GQA);
+//   * KV tiles of 64 keys are gathered from the paged cache through the block
+//     table with direct-to-LDS 16-byte loads (global_load_lds_dwordx4), double
+//     buffered: the loads of tile t+1 and the block-table reads of tile t+2 are
+//     in flight while tile t is computed.  Each load instruction writes whole
+//     rows as one block and blocks are padded (K by 16 bytes, V by 64), so the
+//     K reads below and the transposed V reads hit distinct banks while every
+//     LDS address stays a lane base plus an immediate;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K from LDS as the A operand, Q
+//     held in registers as the B operand, so each lane ends up holding 32 scores
+//     of ONE query row (the row's other 32 keys sit in lane ^ 32) and the online
+//     softmax needs a single cross-half exchange per tile;
+//   * O^T += V^T P^T: P^T comes straight from the S^T accumulators (rounded to
+//     bf16), V^T is read out of the row-major V tile with ds_read_b64_tr_b16, and
+//     O^T keeps one query row per lane, so rescaling is per lane;
+//   * the running max is only moved when a tile's max exceeds it by more than
+//     2^8 (log2 units); otherwise P may reach 256, still exact in bf16/fp32, and
+//     the O rescale is skipped for the whole wave;
+//   * per-element masking only on tiles not entirely inside every row's allowed
+//     interval (each row's allowed keys form one interval).
 #include "device_common.h"
 #include "psw_internal.h"
 
 namespace psw {
 
-template <int D, int DV>
+template <int D, int DV, int WAVES>
 struct PrefillShape {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = WAVES;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kRowsPerWave = 32;
   static constexpr int kBlockM = kWaves * kRowsPerWave;
   static constexpr int kTile = 64;
-  static constexpr int kKStride = D + 8;  // LDS row pitch in bf16 (16 B of padding)
-  static constexpr int kVStride = DV + 8;
+  static constexpr int kKChunks = D / 8;   // 16-byte chunks per K row
+  static constexpr int kVChunks = DV / 8;
+  // LDS layout of a tile: one LDS-DMA instruction moves 1 KB = kRowsPerInstr
+  // whole rows (rows g, g + kInstrPerTile, ...), written as one block; blocks
+  // are kKBlock / kVBlock bytes apart.  The 16 extra bytes per K block put 16
+  // consecutive rows read at the same column in 16 distinct bank groups; the
+  // 64 extra bytes per V block do the same for the 4 rows x 4 chunks of a
+  // transposed read.  Every LDS address is a per-lane base plus immediates.
+  static constexpr int kRowsPerInstr = 1024 / (D * 2);
+  static constexpr int kInstrPerTile = kTile / kRowsPerInstr;
+  static constexpr int kInstrPerWave = kInstrPerTile / kWaves;
+  static constexpr int kKBlock = 1024 + 16;
+  static constexpr int kVBlock = 1024 + 64;
   static constexpr int kQFrags = D / 16;
   static constexpr int kOBlocks = DV / 32;
-  static constexpr int kKChunks = kTile * D / 8 / kThreads;
-  static constexpr int kVChunks = kTile * DV / 8 / kThreads;
-  static_assert(kKChunks >= 1 && kVChunks >= 1, "tile too small for the workgroup");
+  static constexpr int kKBytes = kInstrPerTile * kKBlock;
+  static constexpr int kVBytes = kInstrPerTile * kVBlock;
+  static_assert(D == DV, "K and V tiles share the row-to-instruction mapping");
+  static_assert(kRowsPerInstr * D * 2 == 1024 && kInstrPerWave * kWaves == kInstrPerTile,
+                "tile rows must split evenly into LDS-DMA instructions and waves");
+  static_assert(2 * (kKBytes + kVBytes) <= 160 * 1024, "double buffer exceeds LDS");
 };
 
-template <int D, int DV>
-__global__ __launch_bounds__(256) void prefill_attention_kernel(const AttnParams p) {
-  using S = PrefillShape<D, DV>;
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[S::kTile * S::kKStride];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[S::kTile * S::kVStride];
+// Byte offset of tile row r inside a K or V tile buffer.
+template <class S>
+__device__ __forceinline__ int lds_row(int r, int block_bytes) {
+  return (r % S::kInstrPerTile) * block_bytes + (r / S::kInstrPerTile) * (1024 / S::kRowsPerInstr);
+}
+
+__device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(
+      (const __attribute__((address_space(1))) void*)gsrc,
+      (__attribute__((address_space(3))) void*)(lds_void*)lds_dst, 16, 0, 0);
+}
+
+template <int D, int DV, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void prefill_attention_kernel(const AttnParams p) {
+  using S = PrefillShape<D, DV, WAVES>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave, wave = tid / kWave;
@@ -96,6 +128,12 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const AttnParams
       row_hi = (int)hi64;
     }
   }
+  // the wave's common interval: 32-key halves inside it need no per-element mask
+  int wave_lo = row_valid ? row_lo : INT32_MIN, wave_hi = row_valid ? row_hi : INT32_MAX;
+  for (int o = 32; o > 0; o >>= 1) {
+    wave_lo = max(wave_lo, __shfl_xor(wave_lo, o, kWave));
+    wave_hi = min(wave_hi, __shfl_xor(wave_hi, o, kWave));
+  }
 
   bf16x8 qf[S::kQFrags];
   {
@@ -112,116 +150,117 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const AttnParams
   for (int b = 0; b < S::kOBlocks; ++b) o[b] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const bool latent = p.v_cache == p.k_cache;
-  const int64_t k_slot_pitch = (int64_t)p.num_kv_heads * D;
-  const int64_t v_slot_pitch = latent ? k_slot_pitch : (int64_t)p.num_kv_heads * DV;
-  const uint16_t* kbase = p.k_cache + (int64_t)kvh * D;
-  const uint16_t* vbase = p.v_cache + (int64_t)kvh * (latent ? D : DV);
-  const int32_t* bt = p.block_table + (int64_t)seq * p.block_table_stride;
-  const int bs_log2 = p.block_size_log2;
-  const int bs_mask = (1 << bs_log2) - 1;
-  const float c2 = p.scale_log2;
+  if (t_lo < t_hi) {
+    const bool latent = p.v_cache == p.k_cache;
+    const int64_t k_slot_pitch = (int64_t)p.num_kv_heads * D;
+    const int64_t v_slot_pitch = latent ? k_slot_pitch : (int64_t)p.num_kv_heads * DV;
+    const uint16_t* kbase = p.k_cache + (int64_t)kvh * D;
+    const uint16_t* vbase = p.v_cache + (int64_t)kvh * (latent ? D : DV);
+    const int32_t* bt = p.block_table + (int64_t)seq * p.block_table_stride;
+    const int bs_log2 = p.block_size_log2;
+    const int bs_mask = (1 << bs_log2) - 1;
+    const float c2 = p.scale_log2;
 
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int tile_base = t * S::kTile;
-    uint4 kreg[S::kKChunks], vreg[S::kVChunks];
+    // Lane l holds the physical block of key (tile * 64 + l) of the next tile;
+    // keys past the end are clamped to the last key (finite data, masked out).
+    auto fetch_block = [&](int tile) -> int {
+      const int key = min(tile * S::kTile + lane, seq_len - 1);
+      return bt[key >> bs_log2];
+    };
+    // LDS-DMA instruction g moves rows g + kInstrPerTile * q, q = lane / (D / 8),
+    // 16-byte chunk lane % (D / 8) of each, into the block at g * k/vBlock.
+    const int dma_q = lane / (D / 8), dma_ch = lane % (D / 8);
+    auto issue_tile = [&](int tile, int buf, int blk_of_lane) {
+      char* kt = smem + buf * (S::kKBytes + S::kVBytes);
+      char* vt = kt + S::kKBytes;
 #pragma unroll
-    for (int i = 0; i < S::kKChunks; ++i) {
-      const int c = i * S::kThreads + tid;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int key = tile_base + row;
-      kreg[i] = make_uint4(0, 0, 0, 0);
-      if (key < seq_len) {
-        const int64_t slot = ((int64_t)bt[key >> bs_log2] << bs_log2) + (key & bs_mask);
-        kreg[i] = *reinterpret_cast<const uint4*>(kbase + slot * k_slot_pitch + col);
+      for (int i = 0; i < S::kInstrPerWave; ++i) {
+        const int g = wave * S::kInstrPerWave + i;
+        const int row = g + S::kInstrPerTile * dma_q;
+        const int key = min(tile * S::kTile + row, seq_len - 1);
+        const int blk = __shfl(blk_of_lane, row, kWave);
+        const int64_t cache_row = ((int64_t)blk << bs_log2) + (key & bs_mask);
+        lds_dma16(kbase + cache_row * k_slot_pitch + dma_ch * 8, kt + g * S::kKBlock);
+        lds_dma16(vbase + cache_row * v_slot_pitch + dma_ch * 8, vt + g * S::kVBlock);
       }
-    }
-#pragma unroll
-    for (int i = 0; i < S::kVChunks; ++i) {
-      const int c = i * S::kThreads + tid;
-      const int row = c / (DV / 8), col = (c % (DV / 8)) * 8;
-      const int key = tile_base + row;
-      vreg[i] = make_uint4(0, 0, 0, 0);
-      if (key < seq_len) {
-        const int64_t slot = ((int64_t)bt[key >> bs_log2] << bs_log2) + (key & bs_mask);
-        vreg[i] = *reinterpret_cast<const uint4*>(vbase + slot * v_slot_pitch + col);
-      }
-    }
-    __syncthreads();  // every wave is done reading the previous tile
-#pragma unroll
-    for (int i = 0; i < S::kKChunks; ++i) {
-      const int c = i * S::kThreads + tid;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(&k_lds[row * S::kKStride + col]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < S::kVChunks; ++i) {
-      const int c = i * S::kThreads + tid;
-      const int row = c / (DV / 8), col = (c % (DV / 8)) * 8;
-      *reinterpret_cast<uint4*>(&v_lds[row * S::kVStride + col]) = vreg[i];
-    }
-    __syncthreads();
+    };
 
-    // S^T[key][row] for the two 32-key halves of the tile
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
-#pragma unroll
-    for (int c = 0; c < S::kQFrags; ++c) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(
-          &k_lds[(lane & 31) * S::kKStride + c * 16 + half * 8]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(
-          &k_lds[(32 + (lane & 31)) * S::kKStride + c * 16 + half * 8]);
-      s0 = mfma32(a0, qf[c], s0);
-      s1 = mfma32(a1, qf[c], s1);
-    }
-
-    const bool full = tile_base >= row_lo && tile_base + S::kTile - 1 <= row_hi;
-    if (__ballot(!full) != 0) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int k0 = tile_base + (i / 4) * 8 + half * 4 + (i % 4);
-        const int k1 = k0 + 32;
-        s0[i] = (k0 >= row_lo && k0 <= row_hi) ? s0[i] : -INFINITY;
-        s1[i] = (k1 >= row_lo && k1 <= row_hi) ? s1[i] : -INFINITY;
-      }
-    }
-
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-    mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float m_sub = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_sub);
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s0[i] = fast_exp2(fmaf(s0[i], c2, -m_sub));
-      s1[i] = fast_exp2(fmaf(s1[i], c2, -m_sub));
-      psum += s0[i] + s1[i];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int b = 0; b < S::kOBlocks; ++b) o[b] *= alpha;
-
-    bf16x8 pf[2][2];
-    pf[0][0] = to_bf16x8(s0[0], s0[1], s0[2], s0[3], s0[4], s0[5], s0[6], s0[7]);
-    pf[0][1] = to_bf16x8(s0[8], s0[9], s0[10], s0[11], s0[12], s0[13], s0[14], s0[15]);
-    pf[1][0] = to_bf16x8(s1[0], s1[1], s1[2], s1[3], s1[4], s1[5], s1[6], s1[7]);
-    pf[1][1] = to_bf16x8(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
+    int blk_next = fetch_block(t_lo);
+    issue_tile(t_lo, 0, blk_next);
+    if (t_lo + 1 < t_hi) blk_next = fetch_block(t_lo + 1);
 
     const int tr_row = half * 4 + ((lane & 15) >> 2);
-    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-    for (int b = 0; b < S::kOBlocks; ++b) {
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // bf16 column in a 32-block
+
+    for (int t = t_lo; t < t_hi; ++t) {
+      const int buf = (t - t_lo) & 1;
+      // this wave's LDS-DMA loads of tile t and its block-table read have
+      // landed; the barrier extends that to every wave and fences the reads of
+      // the other buffer (tile t-1) before it is refilled
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (t + 1 < t_hi) {
+        issue_tile(t + 1, buf ^ 1, blk_next);
+        if (t + 2 < t_hi) blk_next = fetch_block(t + 2);
+      }
+      const char* kt = smem + buf * (S::kKBytes + S::kVBytes);
+      const char* vt = kt + S::kKBytes;
+
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        const int base = t * S::kTile + kb * 32;
+        // S^T[key][row] for 32 keys
+        f32x16 s = f32x16{};
+        const int kr = kb * 32 + (lane & 31);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int row0 = kb * 32 + 16 * j + tr_row;
-          const __bf16* src = &v_lds[row0 * S::kVStride + b * 32 + tr_col];
-          const bf16x8 a = cat8(lds_read_tr4(src), lds_read_tr4(src + 8 * S::kVStride));
-          o[b] = mfma32(a, pf[kb][j], o[b]);
+        for (int c = 0; c < S::kQFrags; ++c) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              kt + lds_row<S>(kr, S::kKBlock) + (2 * c + half) * 16);
+          s = mfma32(a, qf[c], s);
+        }
+        if (!(base >= wave_lo && base + 31 <= wave_hi)) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int k = base + (i / 4) * 8 + half * 4 + (i % 4);
+            s[i] = (k >= row_lo && k <= row_hi) ? s[i] : -INFINITY;
+          }
+        }
+        float mx = s[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+        mx = fmaxf(mx, swap_halves(mx)) * c2;
+        // move the running max only when it grows by more than 2^8
+        if (__ballot(mx > m_run + 8.f) != 0) {
+          const float m_new = fmaxf(m_run, mx);
+          // 0 when only m_run is -inf; 1 for a row that is still fully masked
+          const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int b = 0; b < S::kOBlocks; ++b) o[b] *= alpha;
+          m_run = m_new;
+        }
+        const float m_sub = m_run == -INFINITY ? 0.f : m_run;
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s[i] = fast_exp2(fmaf(s[i], c2, -m_sub));
+          psum += s[i];
+        }
+        l_run += psum;
+        const bf16x8 pf0 = to_bf16x8(s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]);
+        const bf16x8 pf1 = to_bf16x8(s[8], s[9], s[10], s[11], s[12], s[13], s[14], s[15]);
+#pragma unroll
+        for (int b = 0; b < S::kOBlocks; ++b) {
+          const int col = b * 32 + tr_col;  // bf16 column
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int ra = kb * 32 + 16 * j + tr_row, rb = ra + 8;
+            const bf16x4 lo = lds_read_tr4(reinterpret_cast<const __bf16*>(
+                vt + lds_row<S>(ra, S::kVBlock) + col * 2));
+            const bf16x4 hi = lds_read_tr4(reinterpret_cast<const __bf16*>(
+                vt + lds_row<S>(rb, S::kVBlock) + col * 2));
+            o[b] = mfma32(cat8(lo, hi), j == 0 ? pf0 : pf1, o[b]);
+          }
         }
       }
     }
@@ -262,22 +301,27 @@ bool prefill_supported(int head_dim_qk, int head_dim_v, int queries_per_kv, bool
          (head_dim_qk == 64 || head_dim_qk == 128 || head_dim_qk == 256);
 }
 
-template <int D, int DV>
+template <int D, int DV, int WAVES>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
-  using S = PrefillShape<D, DV>;
+  using S = PrefillShape<D, DV, WAVES>;
   const int block_q = S::kBlockM / p.queries_per_kv;
   const int gx = p.num_tokens / block_q + p.num_seqs;
   if (gx == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_attention_kernel<D, DV>), dim3(gx, p.num_kv_heads, p.num_splits),
-                     dim3(S::kThreads), 0, stream, p);
+  const size_t lds = 2 * (S::kKBytes + S::kVBytes);
+  auto kern = prefill_attention_kernel<D, DV, WAVES>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(gx, p.num_kv_heads, p.num_splits), dim3(S::kThreads), lds,
+                     stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_attention_prefill(const AttnParams& p, hipStream_t stream) {
   switch (p.head_dim_qk) {
-    case 64: return launch_prefill_t<64, 64>(p, stream);
-    case 128: return launch_prefill_t<128, 128>(p, stream);
-    case 256: return launch_prefill_t<256, 256>(p, stream);
+    case 64: return launch_prefill_t<64, 64, 8>(p, stream);
+    case 128: return launch_prefill_t<128, 128, 8>(p, stream);
+    case 256: return launch_prefill_t<256, 256, 8>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

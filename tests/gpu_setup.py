@@ -84,7 +84,7 @@ def assert_close(got, ref, what=""):
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     err = np.abs(got - ref)
-    bad = err > ATOL + RTOL * np.abs(ref)
+    bad = ~(err <= ATOL + RTOL * np.abs(ref))   # NaN / inf anywhere is a failure
     if bad.any():
         idx = np.argwhere(bad)[:5]
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements out of tolerance; "
