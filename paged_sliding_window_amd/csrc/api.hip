@@ -6,7 +6,7 @@
 #include <cstring>
 #include <cstdarg>
 
-#include "../../include/psw.h"
+#include "psw.h"
 #include "device_common.h"
 #include "psw_internal.h"
 

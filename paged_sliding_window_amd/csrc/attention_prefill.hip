@@ -81,13 +81,18 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_attention_kernel(const Att
   const int tid = threadIdx.x;
   const int lane = tid % kWave, wave = tid / kWave;
   const int half = lane >> 5;
-  const int kvh = blockIdx.y, split = blockIdx.z;
   const int qpk = p.queries_per_kv;
   const int block_q = S::kBlockM / qpk;
 
   // ---- request and query block of this workgroup --------------------------
-  // Query blocks of request s occupy grid slots [qsl[s] / block_q + s, ...).
-  const int x = blockIdx.x;
+  // Logical work item (x fastest, then KV head, then split), spread so that
+  // each XCD walks consecutive query blocks of one KV head.
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int logical = xcd_logical_id(blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z),
+                                     nx * ny * gridDim.z);
+  const int x = logical % nx;
+  const int kvh = (logical / nx) % ny, split = logical / (nx * ny);
+  // Query blocks of request s occupy slots [qsl[s] / block_q + s, ...) of x.
   int s_lo = 0, s_hi = p.num_seqs - 1;
   while (s_lo < s_hi) {
     const int mid = (s_lo + s_hi + 1) >> 1;

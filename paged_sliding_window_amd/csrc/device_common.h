@@ -74,6 +74,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Workgroups are handed to the 8 XCDs round-robin by linear id (id % 8), and
+// each XCD has its own L2.  This bijection gives XCD x the contiguous range of
+// logical ids [x * q + min(x, r), ...) (q = n / 8, r = n % 8), so neighbouring
+// logical work items, which read overlapping K/V, share one L2.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ int xcd_logical_id(int lin, int n) {
+  const int xcd = lin % kNumXcd, local = lin / kNumXcd;
+  const int q = n / kNumXcd, r = n % kNumXcd;
+  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
 __device__ __forceinline__ float swap_halves(float x) {  // value of lane l ^ 32
   return __shfl_xor(x, 32, kWave);
 }
