@@ -3,14 +3,18 @@
 // (vLLM PR #53147 summary, "Implementation breakdown" and "Key source snippet").
 //
 // Work decomposition (gfx950, wave64):
-//   * one workgroup = one query block x one KV head x one key split; WAVES waves
-//     of 32 rows each.  Rows are (position, query head of this KV head) in
+//   * one workgroup = one query block x one KV head x one key split; 4 waves of
+//     32 rows each.  Rows are (position, query head of this KV head) in
 //     position-major order, so one K/V tile in LDS serves every query head that
-//     shares it (GQA);
-//   * KV tiles of 64 keys are gathered from the paged cache through the block
+//     shares it (GQA).  Workgroups are ordered so each XCD walks consecutive
+//     query blocks of one KV head (their K/V windows overlap);
+//   * two workgroups share a CU, so each SIMD runs two waves whose tile
+//     barriers are independent: one wave's softmax overlaps the other's MFMAs
+//     (a single 8-wave workgroup keeps both waves of a SIMD in the same phase);
+//   * KV tiles of 32 keys are gathered from the paged cache through the block
 //     table with direct-to-LDS 16-byte loads (global_load_lds_dwordx4), double
-//     buffered: the loads of tile t+1 and the block-table reads of tile t+2 are
-//     in flight while tile t is computed.  Each load instruction writes whole
+//     buffered (68 KB per workgroup at head dim 256): the loads of tile t+1 and
+//     the block-table reads of tile t+2 are in flight while tile t is computed.  Each load instruction writes whole
 //     rows as one block and blocks are padded (K by 16 bytes, V by 64), so the
 //     K reads below and the transposed V reads hit distinct banks while every
 //     LDS address stays a lane base plus an immediate;
@@ -31,13 +35,13 @@
 
 namespace psw {
 
-template <int D, int DV, int WAVES>
+template <int D, int DV>
 struct PrefillShape {
-  static constexpr int kWaves = WAVES;
+  static constexpr int kWaves = 4;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kRowsPerWave = 32;
   static constexpr int kBlockM = kWaves * kRowsPerWave;
-  static constexpr int kTile = 64;
+  static constexpr int kTile = 32;
   static constexpr int kKChunks = D / 8;   // 16-byte chunks per K row
   static constexpr int kVChunks = DV / 8;
   // LDS layout of a tile: one LDS-DMA instruction moves 1 KB = kRowsPerInstr
@@ -73,9 +77,10 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_dst) {
       (__attribute__((address_space(3))) void*)(lds_void*)lds_dst, 16, 0, 0);
 }
 
-template <int D, int DV, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void prefill_attention_kernel(const AttnParams p) {
-  using S = PrefillShape<D, DV, WAVES>;
+template <int D, int DV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void
+prefill_attention_kernel(const AttnParams p) {
+  using S = PrefillShape<D, DV>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(WAVES * 64) void prefill_attention_kernel(const Att
       const char* vt = kt + S::kKBytes;
 
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < S::kTile / 32; ++kb) {
         const int base = t * S::kTile + kb * 32;
         // S^T[key][row] for 32 keys
         f32x16 s = f32x16{};
@@ -306,14 +311,14 @@ bool prefill_supported(int head_dim_qk, int head_dim_v, int queries_per_kv, bool
          (head_dim_qk == 64 || head_dim_qk == 128 || head_dim_qk == 256);
 }
 
-template <int D, int DV, int WAVES>
+template <int D, int DV>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
-  using S = PrefillShape<D, DV, WAVES>;
+  using S = PrefillShape<D, DV>;
   const int block_q = S::kBlockM / p.queries_per_kv;
   const int gx = p.num_tokens / block_q + p.num_seqs;
   if (gx == 0) return hipSuccess;
   const size_t lds = 2 * (S::kKBytes + S::kVBytes);
-  auto kern = prefill_attention_kernel<D, DV, WAVES>;
+  auto kern = prefill_attention_kernel<D, DV>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
@@ -324,9 +329,9 @@ static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
 
 hipError_t launch_attention_prefill(const AttnParams& p, hipStream_t stream) {
   switch (p.head_dim_qk) {
-    case 64: return launch_prefill_t<64, 64, 8>(p, stream);
-    case 128: return launch_prefill_t<128, 128, 8>(p, stream);
-    case 256: return launch_prefill_t<256, 256, 8>(p, stream);
+    case 64: return launch_prefill_t<64, 64>(p, stream);
+    case 128: return launch_prefill_t<128, 128>(p, stream);
+    case 256: return launch_prefill_t<256, 256>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
