@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--skip-decode", action="store_true", help="omit the decode half")
     ap.add_argument("--decode-splits", type=int, default=8)
+    ap.add_argument("--decode-partials", choices=["f32", "bf16"], default="bf16",
+                    help="dtype of the history/current partial outputs")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="first run one plain device copy of this many bytes (a known-size "
                          "kernel to calibrate HBM byte counters against)")
@@ -226,11 +228,54 @@ def main():
         log("decode half")
         result["decode"] = bench_decode(args, torch, psw, np)
 
+    log("slot mapping, scaled batch")
+    result["slot_mapping_scaled"] = bench_slot_mapping(torch, psw, np)
     if not args.skip_cpu:
         log("CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(w)
     result["setup_s"] = round(time.perf_counter() - t_setup, 1)
     print(json.dumps(result), flush=True)
+
+
+def bench_slot_mapping(torch, psw, np, num_reqs=4096, seed=7):
+    """Slot mapping over a large synthetic batch (not one of the workloads: at
+    their sizes the kernel moves under 0.3 MB and only latency shows).
+    Algorithmic bytes: 8 B position read + 4 B slot written per token, the
+    block-table entries of the blocks touched, and 4 B per pad slot."""
+    from tests.gpu_setup import i32, i64
+    rng = np.random.default_rng(seed)
+    B = 16
+    lens = rng.integers(512, 2049, size=num_reqs)
+    need = -(-lens // B)
+    stride = int(need.max())
+    bt = np.full((num_reqs, stride), -1, dtype=np.int32)
+    perm = rng.permutation(int(need.sum())).astype(np.int32)
+    off = 0
+    for r in range(num_reqs):
+        bt[r, :need[r]] = perm[off:off + need[r]]
+        off += need[r]
+    qsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    pos = np.concatenate([np.arange(L) for L in lens]).astype(np.int64)
+    n = int(qsl[-1])
+    m = n + 65536
+    d_qsl, d_pos, d_bt = i32(qsl), i64(pos), i32(bt)
+    out = torch.empty(m, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        psw.slot_mapping(d_qsl, d_pos, d_bt, B, m, out=out)
+    torch.cuda.synchronize()
+    reps = 50
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        psw.slot_mapping(d_qsl, d_pos, d_bt, B, m, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    alg = n * 12 + int(need.sum()) * 4 + (m - n) * 4
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {"tokens": n, "max_num_tokens": m, "requests": num_reqs, "block_size": B,
+            "ms": round(ms, 5), "algorithmic_bytes": alg, "GBps": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def bench_decode(args, torch, psw, np):
@@ -259,9 +304,10 @@ def bench_decode(args, torch, psw, np):
     kr_hist = i32(w.key_ranges)
     kr_cur = i32(w.current_ranges)
     S = w.key_ranges.shape[0]
-    hist_o = torch.empty((S, R, H, DV), dtype=torch.float32, device="cuda")
+    pdt = torch.float32 if args.decode_partials == "f32" else torch.bfloat16
+    hist_o = torch.empty((S, R, H, DV), dtype=pdt, device="cuda")
     hist_l = torch.empty((S, R, H), dtype=torch.float32, device="cuda")
-    cur_o = torch.empty((1, R, H, DV), dtype=torch.float32, device="cuda")
+    cur_o = torch.empty((1, R, H, DV), dtype=pdt, device="cuda")
     cur_l = torch.empty((1, R, H), dtype=torch.float32, device="cuda")
     out = torch.empty((R * H, DV), dtype=torch.bfloat16, device="cuda")
     slots = torch.empty(R, dtype=torch.int32, device="cuda")
@@ -277,10 +323,10 @@ def bench_decode(args, torch, psw, np):
             ev[i][0].record()
         psw.swa_mm_attention(q, cache, None, bt, qsl, seq_lens, scale=w.scale, window=0,
                              causal=True, key_ranges=kr_hist, head_dim_v=DV, out=hist_o,
-                             lse=hist_l, out_dtype=torch.float32)
+                             lse=hist_l, out_dtype=pdt)
         psw.swa_mm_attention(q, cache, None, bt, qsl, seq_lens, scale=w.scale, window=0,
                              causal=True, key_ranges=kr_cur, head_dim_v=DV, out=cur_o,
-                             lse=cur_l, out_dtype=torch.float32)
+                             lse=cur_l, out_dtype=pdt)
         if i is not None:
             ev[i][1].record()
         psw.lse_combine(outs, lses, out=out)
@@ -316,6 +362,7 @@ def bench_decode(args, torch, psw, np):
         "attention_GBps": round(attn_gbs, 1),
         "combine_ms": round(comb_ms, 5),
         "history_splits": S,
+        "partial_dtype": args.decode_partials,
         "step": "slot_mapping + kv_cache_write + history and current partials + lse_combine",
     }
 
