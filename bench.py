@@ -98,7 +98,7 @@ def cpu_baseline(w):
                       f"{passes} pass(es) in {dt:.2f} s"}
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_attention_gemma16550_traffic.json")
 PREFILL_SOURCES = ["attention_prefill.hip", "device_common.h", "mask_bounds.h", "psw_internal.h"]
 
 
