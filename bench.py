@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--skip-decode", action="store_true", help="omit the decode half")
-    ap.add_argument("--decode-splits", type=int, default=8)
+    ap.add_argument("--decode-splits", type=int, default=1)
     ap.add_argument("--decode-partials", choices=["f32", "bf16"], default="bf16",
                     help="dtype of the history/current partial outputs")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -313,6 +313,13 @@ def bench_decode(args, torch, psw, np):
     slots = torch.empty(R, dtype=torch.int32, device="cuda")
     outs = [hist_o[j].view(R * H, DV) for j in range(S)] + [cur_o[0].view(R * H, DV)]
     lses = [hist_l[j].view(R * H) for j in range(S)] + [cur_l[0].view(R * H)]
+    # one workspace for both attention calls (they run in order on one stream)
+    ws_args = psw.ops._attn_args(q, cache, None, bt, qsl, seq_lens, scale=w.scale, window=0,
+                                 causal=True, chunk_size=0, chunk_lookback=-1, mm_ranges=None,
+                                 key_ranges=kr_hist, out=hist_o, lse=hist_l, head_dim_v=DV,
+                                 out_dtype=0, num_splits=S)
+    ws = torch.empty(max(1, psw.ops.attention_workspace_size(ws_args)), dtype=torch.uint8,
+                     device="cuda")
     steps = max(args.steps, 10)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
 
@@ -323,10 +330,10 @@ def bench_decode(args, torch, psw, np):
             ev[i][0].record()
         psw.swa_mm_attention(q, cache, None, bt, qsl, seq_lens, scale=w.scale, window=0,
                              causal=True, key_ranges=kr_hist, head_dim_v=DV, out=hist_o,
-                             lse=hist_l, out_dtype=pdt)
+                             lse=hist_l, out_dtype=pdt, workspace=ws)
         psw.swa_mm_attention(q, cache, None, bt, qsl, seq_lens, scale=w.scale, window=0,
                              causal=True, key_ranges=kr_cur, head_dim_v=DV, out=cur_o,
-                             lse=cur_l, out_dtype=pdt)
+                             lse=cur_l, out_dtype=pdt, workspace=ws)
         if i is not None:
             ev[i][1].record()
         psw.lse_combine(outs, lses, out=out)

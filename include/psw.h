@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define PSW_ABI_VERSION 1
+#define PSW_ABI_VERSION 2
 
 enum psw_status {
   PSW_OK = 0,
@@ -136,6 +136,9 @@ typedef struct psw_attn_args {
   int32_t num_splits;             /* >= 1; must be 1 when key_ranges == NULL */
   int32_t out_dtype;              /* PSW_BF16 or PSW_F32 */
   float scale;                    /* softmax scale */
+  void* workspace;                /* device scratch of >= psw_attention_workspace_size() bytes,
+                                     256-byte aligned; may be NULL when that size is 0 */
+  int64_t workspace_bytes;        /* size of workspace */
 } psw_attn_args;
 
 /*
@@ -151,9 +154,24 @@ typedef struct psw_attn_args {
  * Errors: PSW_ERR_INVALID (struct_size mismatch, counts < 0, num_q_heads not a
  * multiple of num_kv_heads, block_size not a power of two, chunk_size < 1 with
  * chunk_lookback >= 0, num_splits < 1, num_splits > 1 without key_ranges, NULL
- * pointer), PSW_ERR_UNSUPPORTED (head dims / dtype combination without a kernel).
+ * pointer, workspace missing, misaligned or smaller than
+ * psw_attention_workspace_size()), PSW_ERR_UNSUPPORTED (head dims / dtype
+ * combination without a kernel).
  */
 int psw_swa_mm_attention(const psw_attn_args* args, void* stream);
+
+/*
+ * psw_attention_workspace_size - bytes of device workspace psw_swa_mm_attention
+ * needs for these arguments on the calling thread's current device (stored in
+ * *bytes; 0 when the call needs none).  Today only the latent decode uses it:
+ * it balances all (token, split) items over one workgroup per CU and keeps the
+ * per-item tile prefix and the pieces of items shared by several workgroups
+ * there.  The size depends on num_tokens, num_splits, num_q_heads and the CU
+ * count, not on device data.  The workspace holds no state between calls, but
+ * two calls that overlap in time must not share one.
+ * Errors: as psw_swa_mm_attention's argument checks; bytes == NULL is PSW_ERR_INVALID.
+ */
+int psw_attention_workspace_size(const psw_attn_args* args, int64_t* bytes);
 
 /*
  * psw_lse_combine - [DCP] "Terms", section 1.1 and code block D: merge P partial

@@ -5,6 +5,7 @@ every step of the path runs in the library's HIP kernels; this module only
 checks tensor metadata and passes device pointers and the current stream.
 """
 from .ops import (  # noqa: F401
+    attention_workspace_size,
     kv_cache_write,
     lse_combine,
     slot_mapping,

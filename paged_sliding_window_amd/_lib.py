@@ -39,6 +39,7 @@ class PswAttnArgs(ctypes.Structure):
         ("window", _i32), ("causal", _i32), ("chunk_size", _i32), ("chunk_lookback", _i32),
         ("num_splits", _i32), ("out_dtype", _i32),
         ("scale", ctypes.c_float),
+        ("workspace", _vp), ("workspace_bytes", _i64),
     ]
 
 
@@ -49,6 +50,7 @@ EXPORTS = {
     "psw_slot_mapping": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _i32, _vp]),
     "psw_kv_cache_write": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _vp]),
     "psw_swa_mm_attention": (_i32, [ctypes.POINTER(PswAttnArgs), _vp]),
+    "psw_attention_workspace_size": (_i32, [ctypes.POINTER(PswAttnArgs), ctypes.POINTER(_i64)]),
     "psw_lse_combine": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _i32, _i64, _i32,
                                _vp, _i32, _vp, _vp]),
     "psw_tile_bounds": (_i32, [ctypes.POINTER(PswAttnArgs), _i32, _i32, _i32, _vp, _vp, _i32,

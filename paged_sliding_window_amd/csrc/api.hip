@@ -105,7 +105,8 @@ int psw_kv_cache_write(const void* k_new, const void* v_new, const int32_t* slot
                    "kv_cache_write");
 }
 
-static int fill_geometry(const psw_attn_args* a, psw::AttnParams& p, bool need_tensors) {
+static int fill_geometry(const psw_attn_args* a, psw::AttnParams& p, bool need_tensors,
+                         bool need_pointers = true) {
   if (a == nullptr) return fail(PSW_ERR_INVALID, "args is NULL");
   if (a->struct_size != (int32_t)sizeof(psw_attn_args))
     return fail(PSW_ERR_INVALID, "struct_size %d != sizeof(psw_attn_args) %d", a->struct_size,
@@ -121,7 +122,7 @@ static int fill_geometry(const psw_attn_args* a, psw::AttnParams& p, bool need_t
   if (a->chunk_lookback >= 0 && a->chunk_size < 1)
     return fail(PSW_ERR_INVALID, "chunk_size %d must be >= 1 with chunk_lookback %d",
                 a->chunk_size, a->chunk_lookback);
-  if (a->num_seqs > 0 && (a->query_start_loc == nullptr || a->seq_lens == nullptr))
+  if (need_pointers && a->num_seqs > 0 && (a->query_start_loc == nullptr || a->seq_lens == nullptr))
     return fail(PSW_ERR_INVALID, "query_start_loc and seq_lens are required");
   if (need_tensors) {
     if (a->head_dim_qk < 16 || a->head_dim_v < 16)
@@ -136,7 +137,7 @@ static int fill_geometry(const psw_attn_args* a, psw::AttnParams& p, bool need_t
       return fail(PSW_ERR_INVALID, "out_dtype %d unknown", a->out_dtype);
     if (!(a->scale > 0.f) || !std::isfinite(a->scale))
       return fail(PSW_ERR_INVALID, "scale must be finite and > 0");
-    if (a->num_tokens > 0 && (a->q == nullptr || a->k_cache == nullptr ||
+    if (need_pointers && a->num_tokens > 0 && (a->q == nullptr || a->k_cache == nullptr ||
                               a->block_table == nullptr || a->out == nullptr))
       return fail(PSW_ERR_INVALID, "q, k_cache, block_table and out are required");
   }
@@ -170,14 +171,38 @@ static int fill_geometry(const psw_attn_args* a, psw::AttnParams& p, bool need_t
   return PSW_OK;
 }
 
+// Workspace the call needs for these arguments on the current device (0: none).
+static int64_t workspace_needed(const psw_attn_args* args, const psw::AttnParams& p) {
+  const bool latent = args->v_cache == nullptr;
+  if (latent && psw::decode_supported(p) && p.num_tokens > 0 && p.num_seqs > 0)
+    return psw::decode_workspace_bytes(p);
+  return 0;
+}
+
+int psw_attention_workspace_size(const psw_attn_args* args, int64_t* bytes) {
+  if (bytes == nullptr) return fail(PSW_ERR_INVALID, "bytes is NULL");
+  psw::AttnParams p{};
+  int st = fill_geometry(args, p, true, false);
+  if (st != PSW_OK) return st;
+  *bytes = workspace_needed(args, p);
+  return ok();
+}
+
 int psw_swa_mm_attention(const psw_attn_args* args, void* stream) {
   psw::AttnParams p{};
   int st = fill_geometry(args, p, true);
   if (st != PSW_OK) return st;
   const bool latent = args->v_cache == nullptr;
   if (p.num_tokens == 0 || p.num_seqs == 0) return ok();
+  const int64_t need = workspace_needed(args, p);
+  if (need > 0 && (args->workspace == nullptr || args->workspace_bytes < need ||
+                   (reinterpret_cast<uintptr_t>(args->workspace) & 255) != 0))
+    return fail(PSW_ERR_INVALID,
+                "workspace of %lld bytes (256-byte aligned) required, got %lld at %p",
+                (long long)need, (long long)args->workspace_bytes, args->workspace);
   if (latent && psw::decode_supported(p))
-    return check_hip(psw::launch_attention_decode(p, (hipStream_t)stream), "attention(decode)");
+    return check_hip(psw::launch_attention_decode(p, args->workspace, (hipStream_t)stream),
+                     "attention(decode)");
   if (psw::prefill_supported(p.head_dim_qk, p.head_dim_v, p.queries_per_kv, latent))
     return check_hip(psw::launch_attention_prefill(p, (hipStream_t)stream), "attention(prefill)");
   return fail(PSW_ERR_UNSUPPORTED,

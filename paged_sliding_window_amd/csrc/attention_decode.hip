@@ -4,8 +4,22 @@
 // sections 1.1 and 3.1 for the history/current partials that each emit an
 // output and an LSE; code blocks B and C for the two partial calls).
 //
-// One workgroup = one new token x NHB * 32 query heads x one key split, with
-// two waves per 32-head block:
+// Work items are (new token, key split) pairs; item i owns the KV tiles of its
+// query row inside its split's key range.  Decode batches mix requests whose
+// lengths differ by 8x, so one workgroup per item leaves most CUs idle while
+// the longest items finish.  Instead the launch is balanced over the global
+// tile sequence (items in order, each item's tiles in order):
+//   1. decode_plan_kernel writes the exclusive prefix sum of tiles per item;
+//   2. workgroup w of G takes the tiles [w * per, (w + 1) * per), per = ceil(T / G),
+//      which may cover the end of one item, whole items and the start of another.
+//      An item that lies inside one workgroup's range is written to the output
+//      directly; otherwise each workgroup writes its piece (normalised O in fp32
+//      and its LSE) to workspace slot 2w (the item began before the range) or
+//      2w + 1 (the item begins inside the range and continues past it);
+//   3. decode_merge_kernel merges the pieces of every item that spans several
+//      workgroups by their LSEs, and writes 0 / -inf for items without tiles.
+//
+// Inside a workgroup (NHB * 32 query heads, two waves per 32-head block):
 //   * tiles of 32 keys are gathered once per workgroup into LDS with
 //     direct-to-LDS 16-byte loads, double buffered (tile t+1 and the block-table
 //     reads of tile t+2 are in flight while tile t is computed).  LDS-DMA
@@ -21,7 +35,7 @@
 //     the same K tile with ds_read_b64_tr_b16;
 //   * the running max moves only when it grows by more than 2^8 (log2 units).
 // The mask (window, image ranges, key range of the split) is applied exactly
-// as in the prefill kernel; one query position per workgroup makes it uniform.
+// as in the prefill kernel; one query position per item makes it uniform.
 #include "device_common.h"
 #include "psw_internal.h"
 
@@ -35,7 +49,102 @@ constexpr int kHalfChunks = kKChunks / 2;   // 18 per wave of a pair
 constexpr int kBlock = 1024 + 128;          // LDS bytes per k-chunk block (padded)
 constexpr int kTileBytes = kKChunks * kBlock;
 constexpr int kOBlocks = kDV / 2 / 32;      // 8 blocks of 32 output columns per wave
+constexpr int kPlanThreads = 1024;
 }  // namespace dec
+
+#ifndef DEC_NB
+#define DEC_NB 1
+#endif
+
+// One (token, split) work item: its request and the tiles / keys its row may see.
+struct DecodeItem {
+  int token, split, seq, seq_len, t_lo, t_hi, row_lo, row_hi;
+};
+
+__device__ __forceinline__ DecodeItem decode_item(const AttnParams& p, int item) {
+  DecodeItem d;
+  d.token = item / p.num_splits;
+  d.split = item - d.token * p.num_splits;
+  int s_lo = 0, s_hi = p.num_seqs - 1;
+  while (s_lo < s_hi) {
+    const int mid = (s_lo + s_hi + 1) >> 1;
+    if (p.query_start_loc[mid] <= d.token) s_lo = mid; else s_hi = mid - 1;
+  }
+  d.seq = s_lo;
+  const int q_start = p.query_start_loc[d.seq];
+  const int query_len = p.query_start_loc[d.seq + 1] - q_start;
+  const int qpos = d.token - q_start;
+  d.seq_len = p.seq_lens[d.seq];
+  const int ctx = d.seq_len - query_len;
+  const int32_t* ranges =
+      p.mm_ranges ? p.mm_ranges + (int64_t)d.seq * p.max_mm_ranges * 2 : nullptr;
+  int key_begin = 0, key_end = d.seq_len;
+  if (p.key_ranges) {
+    const int64_t kr = ((int64_t)d.split * p.num_seqs + d.seq) * 2;
+    key_begin = max(0, p.key_ranges[kr]);
+    key_end = min(d.seq_len, p.key_ranges[kr + 1]);
+  }
+  int64_t lo64, hi64;
+  row_interval((int64_t)ctx + qpos, d.seq_len, p.geom, ranges, p.max_mm_ranges, key_begin,
+               key_end, lo64, hi64);
+  if (lo64 <= hi64) {
+    // the row's allowed keys are one interval; its tiles are inside the query
+    // block's tile bounds, which are kept as the outer limit
+    const TileRange tr = tile_bounds(ctx, d.seq_len, query_len, qpos, dec::kTile,
+                                     p.queries_per_kv, 1, p.queries_per_kv, p.geom, ranges,
+                                     p.max_mm_ranges);
+    d.row_lo = (int)lo64;
+    d.row_hi = (int)hi64;
+    d.t_lo = max(tr.lo, d.row_lo / dec::kTile);
+    d.t_hi = min(tr.hi, d.row_hi / dec::kTile + 1);
+  } else {
+    d.row_lo = INT32_MAX;
+    d.row_hi = INT32_MIN;
+    d.t_lo = d.t_hi = 0;
+  }
+  if (d.t_hi < d.t_lo) d.t_hi = d.t_lo;
+  return d;
+}
+
+// prefix[i] = number of tiles of items 0..i-1, prefix[items] = total (one workgroup).
+__global__ __launch_bounds__(dec::kPlanThreads) void decode_plan_kernel(const AttnParams p,
+                                                                        int32_t* prefix) {
+  constexpr int kWaves = dec::kPlanThreads / kWave;
+  __shared__ int wave_sum[kWaves];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int items = p.num_tokens * p.num_splits;
+  int carry = 0;
+  for (int base = 0; base < items; base += dec::kPlanThreads) {
+    const int it = base + tid;
+    int cnt = 0;
+    if (it < items) {
+      const DecodeItem d = decode_item(p, it);
+      cnt = d.t_hi - d.t_lo;
+    }
+    int x = cnt;  // inclusive scan inside the wave
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(x, off, kWave);
+      if (lane >= off) x += y;
+    }
+    if (lane == kWave - 1) wave_sum[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+      int v = lane < kWaves ? wave_sum[lane] : 0;
+#pragma unroll
+      for (int off = 1; off < kWaves; off <<= 1) {
+        const int y = __shfl_up(v, off, kWave);
+        if (lane >= off) v += y;
+      }
+      if (lane < kWaves) wave_sum[lane] = v;
+    }
+    __syncthreads();
+    if (it < items) prefix[it] = carry + (wave > 0 ? wave_sum[wave - 1] : 0) + x - cnt;
+    carry += wave_sum[kWaves - 1];
+    __syncthreads();
+  }
+  if (tid == 0) prefix[items] = carry;
+}
 
 // Slot (16 bytes) of key row r, column half hh (columns 8*hh..8*hh+7 of a
 // k-chunk) inside a k-chunk block.  Rows of the second half are rotated by 4 so
@@ -48,148 +157,220 @@ __device__ __forceinline__ void dec_dma16(const void* gsrc, void* lds_dst) {
       (__attribute__((address_space(3))) void*)(lds_void*)lds_dst, 16, 0, 0);
 }
 
-template <int NHB>
-__global__ __launch_bounds__(NHB * 128) void decode_attention_kernel(const AttnParams p) {
+// Where the stream-K pieces live inside the caller's workspace.
+struct DecodeWork {
+  const int32_t* prefix;  // [items + 1]
+  float* piece_o;         // [groups][2 * grid][heads per group][kDV]
+  float* piece_lse;       // [groups][2 * grid][heads per group]
+  int grid;               // workgroups per head group
+};
+
+// Workgroup barrier for LDS data: this wave's LDS reads and writes retire
+// (lgkmcnt) before the barrier, and the memory clobber keeps the compiler from
+// moving memory accesses across it.  Unlike __syncthreads() it does not wait
+// for vector-memory operations, so LDS-DMA tile prefetches stay in flight; a
+// tile's own DMA is waited for with an explicit vmcnt before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left alone).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+__device__ __forceinline__ int load_uniform_i32(const int32_t* ptr) {
+  return *(const __attribute__((address_space(4))) int32_t*)ptr;
+}
+
+// NB: 32-head MFMA blocks per wave; HG: head groups per workgroup.  The
+// workgroup has 2 * HG waves, wave (hg, dh) owns heads [hg * NB * 32, +NB * 32)
+// of the group and the d-half dh; one wave per SIMD, so each wave has the whole
+// register file (the O accumulators live in AGPRs).  UNIFORM_BT: the block size
+// is >= 32, so every 32-key tile lies inside one KV block whose table entry is
+// read with one scalar load; the tile ring is then three deep.
+template <int NB, int HG, bool UNIFORM_BT>
+__global__ __launch_bounds__(HG * 128)
+__attribute__((amdgpu_waves_per_eu((HG * 2 + 3) / 4, (HG * 2 + 3) / 4)))
+void decode_attention_kernel(const AttnParams p, const DecodeWork wk) {
   using namespace dec;
-  constexpr int kWaves = 2 * NHB;
+  constexpr int kWaves = 2 * HG;
+  constexpr int kHeads = HG * NB * 32;              // heads per workgroup
+  // LDS-DMA instructions per tile: waves below kDmaExtra issue one more
+  constexpr int kDmaPerWave = kKChunks / kWaves;
+  constexpr int kDmaExtra = kKChunks % kWaves;
+  constexpr int kBufs = UNIFORM_BT ? 3 : 2;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  float* xs = reinterpret_cast<float*>(smem + 2 * kTileBytes);  // [kWaves][4][64][4]
+  float* xs = reinterpret_cast<float*>(smem + kBufs * kTileBytes);  // [wave][NB][4][64][4]
 
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: keep it scalar
   const int half = lane >> 5;
-  const int hb = wave >> 1, dh = wave & 1;
-  const int token = blockIdx.x;
-  const int head0 = blockIdx.y * (NHB * 32);
-  const int split = blockIdx.z;
-  const int qpk = p.queries_per_kv;
-  const int kvh = head0 / qpk;
+  const int hg = wave >> 1, dh = wave & 1;
+  const int G = wk.grid;
+  const int groups = gridDim.y;
+  const int logical = xcd_logical_id(blockIdx.x + gridDim.x * blockIdx.y, G * groups);
+  const int w = logical % G;       // neighbouring w share items: keep them on one XCD
+  const int group = logical / G;
+  const int head0 = group * kHeads;
+  const int kvh = head0 / p.queries_per_kv;
 
-  int s_lo = 0, s_hi = p.num_seqs - 1;
-  while (s_lo < s_hi) {
-    const int mid = (s_lo + s_hi + 1) >> 1;
-    if (p.query_start_loc[mid] <= token) s_lo = mid; else s_hi = mid - 1;
-  }
-  const int seq = s_lo;
-  const int q_start = p.query_start_loc[seq];
-  const int query_len = p.query_start_loc[seq + 1] - q_start;
-  const int qpos = token - q_start;
-  const int seq_len = p.seq_lens[seq];
-  const int ctx = seq_len - query_len;
-  const int32_t* ranges = p.mm_ranges ? p.mm_ranges + (int64_t)seq * p.max_mm_ranges * 2 : nullptr;
-  int key_begin = 0, key_end = seq_len;
-  if (p.key_ranges) {
-    key_begin = max(0, p.key_ranges[((int64_t)split * p.num_seqs + seq) * 2]);
-    key_end = min(seq_len, p.key_ranges[((int64_t)split * p.num_seqs + seq) * 2 + 1]);
-  }
-  const TileRange tr = tile_bounds(ctx, seq_len, query_len, qpos, kTile, qpk, 1, qpk, p.geom,
-                                   ranges, p.max_mm_ranges);
-  const int t_lo = max(tr.lo, key_begin / kTile);
-  const int t_hi = min(tr.hi, (key_end + kTile - 1) / kTile);
-
-  int row_lo = INT32_MAX, row_hi = INT32_MIN;
+  const int items = p.num_tokens * p.num_splits;
+  const int total = wk.prefix[items];
+  const int per = max(1, (total + G - 1) / G);
+  const int g0 = w * per, g1 = min(total, g0 + per);
+  if (g0 >= g1) return;
+  // first item with tiles at or after g0: the last item whose prefix is <= g0
+  int it;
   {
-    int64_t lo64, hi64;
-    row_interval((int64_t)ctx + qpos, seq_len, p.geom, ranges, p.max_mm_ranges, key_begin,
-                 key_end, lo64, hi64);
-    if (lo64 <= hi64) {
-      row_lo = (int)lo64;
-      row_hi = (int)hi64;
+    int lo = 0, hi = items - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (wk.prefix[mid] <= g0) lo = mid; else hi = mid - 1;
     }
+    it = lo;
   }
 
-  const int head = head0 + hb * 32 + (lane & 31);
-  bf16x8 qf[kHalfChunks];
-  {
-    const uint16_t* qrow =
-        p.q + ((int64_t)token * p.num_q_heads + head) * kD + dh * (kHalfChunks * 16) + half * 8;
+  const int hl0 = hg * NB * 32 + (lane & 31);  // head (inside the group) of block 0
+  const int64_t slot_pitch = (int64_t)p.num_kv_heads * kD;
+  const uint16_t* kbase = p.k_cache + (int64_t)kvh * kD;
+  const int bs_log2 = p.block_size_log2;
+  const int bs_mask = (1 << bs_log2) - 1;
+  const float c2 = p.scale_log2;
+  // this lane's DMA slot: key row and column half within every k-chunk block
+  const int dma_hh = lane >> 5;
+  const int dma_row = (lane - 4 * dma_hh) & 31;
+  // transposed V reads: group of 16 lanes covers 4 keys x 16 columns
+  const int tr_key = half * 4 + ((lane & 15) >> 2);   // + 16 j (+ 8 for the upper 4 keys)
+  const int tr_g = (lane >> 4) & 1;                    // which 16 of a 32-column block
+  const int tr_hh = (lane & 3) >> 1, tr_in = (lane & 1) * 8;
+  const int dcol = dh * (kDV / 2) + half * 4;
+
+  bf16x8 qf[NB][kHalfChunks];
+  int q_token = -1;
+  int g = g0;
+  while (true) {
+    const int p0 = wk.prefix[it], p1 = wk.prefix[it + 1];
+    const DecodeItem d = decode_item(p, it);
+    // previous item: all waves done with LDS, all stores and loads retired
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (d.token != q_token) {
 #pragma unroll
-    for (int c = 0; c < kHalfChunks; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qrow + c * 16);
-  }
-
-  f32x16 o[kOBlocks];
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint16_t* qrow = p.q + ((int64_t)d.token * p.num_q_heads + head0 + hl0 + nb * 32) * kD +
+                               dh * (kHalfChunks * 16) + half * 8;
 #pragma unroll
-  for (int b = 0; b < kOBlocks; ++b) o[b] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+        for (int c = 0; c < kHalfChunks; ++c)
+          qf[nb][c] = *reinterpret_cast<const bf16x8*>(qrow + c * 16);
+      }
+      q_token = d.token;
+    }
+    const int t_first = d.t_lo + (g - p0);
+    const int t_end = d.t_lo + (min(g1, p1) - p0);
+    const int seq_len = d.seq_len;
+    const int row_lo = d.row_lo, row_hi = d.row_hi;
+    const int32_t* bt = p.block_table + (int64_t)d.seq * p.block_table_stride;
 
-  if (t_lo < t_hi) {
-    const int64_t slot_pitch = (int64_t)p.num_kv_heads * kD;
-    const uint16_t* kbase = p.k_cache + (int64_t)kvh * kD;
-    const int32_t* bt = p.block_table + (int64_t)seq * p.block_table_stride;
-    const int bs_log2 = p.block_size_log2;
-    const int bs_mask = (1 << bs_log2) - 1;
-    const float c2 = p.scale_log2;
+    f32x16 o[NB][kOBlocks];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int b = 0; b < kOBlocks; ++b) o[nb][b] = f32x16{};
+    float m_run[NB], l_run[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      m_run[nb] = -INFINITY;
+      l_run[nb] = 0.f;
+    }
 
-    // lane l < 32 holds the physical block of key (tile * 32 + l)
-    auto fetch_block = [&](int tile) -> int {
-      const int key = min(tile * kTile + (lane & 31), seq_len - 1);
-      return bt[key >> bs_log2];
-    };
-    // this lane's DMA slot: key row and column half within every k-chunk block
-    const int dma_hh = lane >> 5;
-    const int dma_row = (lane - 4 * dma_hh) & 31;
-    auto issue_tile = [&](int tile, int buf, int blk_of_lane) {
-      const int key = min(tile * kTile + dma_row, seq_len - 1);
-      const int blk = __shfl(blk_of_lane, dma_row, kWave);
-      const uint16_t* src = kbase + (((int64_t)blk << bs_log2) + (key & bs_mask)) * slot_pitch +
-                            dma_hh * 8;
+    // the LDS-DMA of one tile: this wave moves k-chunks wave, wave + kWaves, ...
+    // Rows past the last key repeat the last key (finite values, masked later).
+    auto issue_tile = [&](int tile, int buf) {
+      const int first = tile * kTile;
+      const uint16_t* src;
+      if constexpr (UNIFORM_BT) {
+        // uniform tile base + a per-lane 32-bit offset (row, column half)
+        const int blk = load_uniform_i32(bt + (first >> bs_log2));
+        const char* tile_base = reinterpret_cast<const char*>(
+            kbase + (((int64_t)blk << bs_log2) + (first & bs_mask)) * slot_pitch);
+        const uint32_t row = (uint32_t)min(dma_row, seq_len - 1 - first);
+        src = reinterpret_cast<const uint16_t*>(
+            tile_base + (row * (uint32_t)slot_pitch + (uint32_t)dma_hh * 8u) * 2u);
+      } else {
+        const int key = min(first + dma_row, seq_len - 1);
+        const int blk = bt[key >> bs_log2];
+        src = kbase + (((int64_t)blk << bs_log2) + (key & bs_mask)) * slot_pitch + dma_hh * 8;
+      }
       char* dst = smem + buf * kTileBytes;
 #pragma unroll
-      for (int i = 0; i < kKChunks / kWaves; ++i) {
+      for (int i = 0; i < kDmaPerWave; ++i) {
         const int c = i * kWaves + wave;
         dec_dma16(src + c * 16, dst + c * kBlock);
       }
-      if constexpr (kKChunks % kWaves != 0) {
-        const int c = (kKChunks / kWaves) * kWaves + wave;
-        if (wave < kKChunks % kWaves) dec_dma16(src + c * 16, dst + c * kBlock);
+      if constexpr (kDmaExtra != 0) {
+        const int c = kDmaPerWave * kWaves + wave;
+        if (wave < kDmaExtra) dec_dma16(src + c * 16, dst + c * kBlock);
       }
     };
 
-    int blk_next = fetch_block(t_lo);
-    issue_tile(t_lo, 0, blk_next);
-    if (t_lo + 1 < t_hi) blk_next = fetch_block(t_lo + 1);
+    issue_tile(t_first, 0);
+    if (kBufs == 3 && t_first + 1 < t_end) issue_tile(t_first + 1, 1);
 
-    // transposed V reads: group of 16 lanes covers 4 keys x 16 columns
-    const int tr_key = half * 4 + ((lane & 15) >> 2);   // + 16 j (+ 8 for the upper 4 keys)
-    const int tr_g = (lane >> 4) & 1;                    // which 16 of a 32-column block
-    const int tr_hh = (lane & 3) >> 1, tr_in = (lane & 1) * 8;
-
-    for (int t = t_lo; t < t_hi; ++t) {
-      const int buf = (t - t_lo) & 1;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (t + 1 < t_hi) {
-        issue_tile(t + 1, buf ^ 1, blk_next);
-        if (t + 2 < t_hi) blk_next = fetch_block(t + 2);
+    for (int t = t_first; t < t_end; ++t) {
+      const int buf = (t - t_first) % kBufs;
+      if constexpr (kBufs == 3) {
+        // tile t landed; tile t + 1 (issued after it) may still be in flight
+        if (t + 1 >= t_end) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        else if (kDmaExtra != 0 && wave < kDmaExtra)
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerWave + 1));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerWave));
+      } else {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       }
+      lds_barrier();
+      // the buffer tile t + kBufs - 1 goes to was last read in iteration t - 1
+      if (t + kBufs - 1 < t_end) issue_tile(t + kBufs - 1, (buf + kBufs - 1) % kBufs);
       const char* kt = smem + buf * kTileBytes;
 
-      f32x16 s = f32x16{};
+      f32x16 s[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
       {
-        const char* arow = kt + dec_slot(lane & 31, half) * 16;
+        const char* arow = kt + dec_slot(lane & 31, half) * 16 + dh * kHalfChunks * kBlock;
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(arow);
 #pragma unroll
         for (int c = 0; c < kHalfChunks; ++c) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + (dh * kHalfChunks + c) * kBlock);
-          s = mfma32(a, qf[c], s);
+          bf16x8 a_next = a;
+          if (c + 1 < kHalfChunks) a_next = *reinterpret_cast<const bf16x8*>(arow + (c + 1) * kBlock);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) s[nb] = mfma32(a, qf[nb][c], s[nb]);
+          a = a_next;
         }
       }
-      // exchange of the two halves: layout [wave][4][lane][4 floats]
+      // exchange of the two d-halves: layout [wave][NB][4][lane][4 floats]
       {
-        f32x4* mine = reinterpret_cast<f32x4*>(xs) + wave * 4 * kWave + lane;
+        f32x4* mine = reinterpret_cast<f32x4*>(xs) + wave * NB * 4 * kWave + lane;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          mine[i * kWave] = f32x4{s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]};
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            mine[(nb * 4 + i) * kWave] =
+                f32x4{s[nb][4 * i], s[nb][4 * i + 1], s[nb][4 * i + 2], s[nb][4 * i + 3]};
       }
-      __syncthreads();
+      lds_barrier();
       {
-        const f32x4* other = reinterpret_cast<const f32x4*>(xs) + (wave ^ 1) * 4 * kWave + lane;
+        const f32x4* other =
+            reinterpret_cast<const f32x4*>(xs) + (wave ^ 1) * NB * 4 * kWave + lane;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 part = other[i * kWave];
-          // both waves of the pair add the halves in the same order
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            s[4 * i + k] = dh == 0 ? s[4 * i + k] + part[k] : part[k] + s[4 * i + k];
-        }
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 part = other[(nb * 4 + i) * kWave];
+            // both waves of the pair add the halves in the same order
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              s[nb][4 * i + k] = dh == 0 ? s[nb][4 * i + k] + part[k] : part[k] + s[nb][4 * i + k];
+          }
       }
 
       const int base = t * kTile;
@@ -197,72 +378,188 @@ __global__ __launch_bounds__(NHB * 128) void decode_attention_kernel(const AttnP
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int k = base + (i / 4) * 8 + half * 4 + (i % 4);
-          s[i] = (k >= row_lo && k <= row_hi) ? s[i] : -INFINITY;
+          const bool ok = k >= row_lo && k <= row_hi;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) s[nb][i] = ok ? s[nb][i] : -INFINITY;
         }
       }
-      float mx = s[0];
+      bf16x8 pf[NB][2];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-      mx = fmaxf(mx, swap_halves(mx)) * c2;
-      if (__ballot(mx > m_run + 8.f) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
+      for (int nb = 0; nb < NB; ++nb) {
+        float mx = s[nb][0];
 #pragma unroll
-        for (int b = 0; b < kOBlocks; ++b) o[b] *= alpha;
-        m_run = m_new;
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[nb][i]);
+        mx = fmaxf(mx, swap_halves(mx)) * c2;
+        if (__ballot(mx > m_run[nb] + 8.f) != 0) {
+          const float m_new = fmaxf(m_run[nb], mx);
+          const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run[nb] - m_new);
+          l_run[nb] *= alpha;
+#pragma unroll
+          for (int b = 0; b < kOBlocks; ++b) o[nb][b] *= alpha;
+          m_run[nb] = m_new;
+        }
+        const float m_sub = m_run[nb] == -INFINITY ? 0.f : m_run[nb];
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s[nb][i] = fast_exp2(fmaf(s[nb][i], c2, -m_sub));
+          psum += s[nb][i];
+        }
+        l_run[nb] += psum;
+        pf[nb][0] = to_bf16x8(s[nb][0], s[nb][1], s[nb][2], s[nb][3], s[nb][4], s[nb][5],
+                              s[nb][6], s[nb][7]);
+        pf[nb][1] = to_bf16x8(s[nb][8], s[nb][9], s[nb][10], s[nb][11], s[nb][12], s[nb][13],
+                              s[nb][14], s[nb][15]);
       }
-      const float m_sub = m_run == -INFINITY ? 0.f : m_run;
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[i] = fast_exp2(fmaf(s[i], c2, -m_sub));
-        psum += s[i];
-      }
-      l_run += psum;
-      const bf16x8 pf0 = to_bf16x8(s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]);
-      const bf16x8 pf1 = to_bf16x8(s[8], s[9], s[10], s[11], s[12], s[13], s[14], s[15]);
 
-#pragma unroll
-      for (int b = 0; b < kOBlocks; ++b) {
-        // output columns dh*256 + b*32 + [0, 32): k-chunk block 2 * (dh*8 + b) + tr_g
-        const char* blk = kt + (2 * (dh * kOBlocks + b) + tr_g) * kBlock + tr_in;
+      // O^T += V^T P^T.  Output columns dh*256 + b*32 + [0, 32) come from
+      // k-chunk block 2 * (dh*8 + b) + tr_g; step st = 2b + j covers keys
+      // [16 j, 16 j + 16).  The two transposed reads of step st + 1 are in
+      // flight while the MFMA of step st runs.
+      {
+        const uint32_t vbase = lds_addr(kt + (2 * dh * kOBlocks + tr_g) * kBlock + tr_in);
+        uint32_t va[2][2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int ka = 16 * j + tr_key, kb2 = ka + 8;
-          const bf16x4 lo = lds_read_tr4(reinterpret_cast<const __bf16*>(blk + dec_slot(ka, tr_hh) * 16));
-          const bf16x4 hi = lds_read_tr4(reinterpret_cast<const __bf16*>(blk + dec_slot(kb2, tr_hh) * 16));
-          o[b] = mfma32(cat8(lo, hi), j == 0 ? pf0 : pf1, o[b]);
+          va[j][0] = vbase + dec_slot(16 * j + tr_key, tr_hh) * 16;
+          va[j][1] = vbase + dec_slot(16 * j + tr_key + 8, tr_hh) * 16;
+        }
+        constexpr int kSteps = 2 * kOBlocks;
+        bf16x4 vr[2][2];
+        vr[0][0] = lds_read_tr4_async(va[0][0]);
+        vr[0][1] = lds_read_tr4_async(va[0][1]);
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+          const int b = st >> 1, j = st & 1, cur = st & 1;
+          if (st + 1 < kSteps) {
+            const int bn = (st + 1) >> 1, jn = (st + 1) & 1;
+            vr[cur ^ 1][0] = lds_read_tr4_async(va[jn][0] + bn * 2 * kBlock);
+            vr[cur ^ 1][1] = lds_read_tr4_async(va[jn][1] + bn * 2 * kBlock);
+            lds_wait_tr<2>(vr[cur][0], vr[cur][1]);
+          } else {
+            lds_wait_tr<0>(vr[cur][0], vr[cur][1]);
+          }
+          const bf16x8 vt = cat8(vr[cur][0], vr[cur][1]);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) o[nb][b] = mfma32(vt, pf[nb][j], o[nb][b]);
         }
       }
     }
-  }
 
-  const float l_tot = l_run + swap_halves(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const int64_t orow = ((int64_t)split * p.num_tokens + token) * p.num_q_heads + head;
-  const int dcol = dh * (kDV / 2) + half * 4;
-  if (p.out_f32) {
-    float* dst = static_cast<float*>(p.out) + orow * kDV + dcol;
+    const bool complete = p0 >= g0 && p1 <= g1;
 #pragma unroll
-    for (int b = 0; b < kOBlocks; ++b)
+    for (int nb = 0; nb < NB; ++nb) {
+      const int hl = hl0 + nb * 32;
+      const float l_tot = l_run[nb] + swap_halves(l_run[nb]);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const float lse_val = l_tot > 0.f ? (m_run[nb] + fast_log2(l_tot)) * kLn2 : -INFINITY;
+      if (complete) {
+        // the whole item is in this workgroup's range: final result
+        const int64_t orow =
+            ((int64_t)d.split * p.num_tokens + d.token) * p.num_q_heads + head0 + hl;
+        if (p.out_f32) {
+          float* dst = static_cast<float*>(p.out) + orow * kDV + dcol;
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(dst + b * 32 + g * 8) =
-            make_float4(o[b][4 * g] * inv, o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv,
-                        o[b][4 * g + 3] * inv);
-  } else {
-    uint16_t* dst = static_cast<uint16_t*>(p.out) + orow * kDV + dcol;
+          for (int b = 0; b < kOBlocks; ++b)
 #pragma unroll
-    for (int b = 0; b < kOBlocks; ++b)
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<float4*>(dst + b * 32 + q * 8) =
+                  make_float4(o[nb][b][4 * q] * inv, o[nb][b][4 * q + 1] * inv,
+                              o[nb][b][4 * q + 2] * inv, o[nb][b][4 * q + 3] * inv);
+        } else {
+          uint16_t* dst = static_cast<uint16_t*>(p.out) + orow * kDV + dcol;
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<bf16x4*>(dst + b * 32 + g * 8) =
-            to_bf16x4(o[b][4 * g] * inv, o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv,
-                      o[b][4 * g + 3] * inv);
+          for (int b = 0; b < kOBlocks; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<bf16x4*>(dst + b * 32 + q * 8) =
+                  to_bf16x4(o[nb][b][4 * q] * inv, o[nb][b][4 * q + 1] * inv,
+                            o[nb][b][4 * q + 2] * inv, o[nb][b][4 * q + 3] * inv);
+        }
+        if (p.lse != nullptr && dh == 0 && half == 0) p.lse[orow] = lse_val;
+      } else {
+        // a piece of an item shared with neighbouring workgroups
+        const int slot = p0 < g0 ? 2 * w : 2 * w + 1;
+        const int64_t prow = ((int64_t)group * 2 * G + slot) * kHeads + hl;
+        float* dst = wk.piece_o + prow * kDV + dcol;
+#pragma unroll
+        for (int b = 0; b < kOBlocks; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(dst + b * 32 + q * 8) =
+                make_float4(o[nb][b][4 * q] * inv, o[nb][b][4 * q + 1] * inv,
+                            o[nb][b][4 * q + 2] * inv, o[nb][b][4 * q + 3] * inv);
+        if (dh == 0 && half == 0) wk.piece_lse[prow] = lse_val;
+      }
+    }
+
+    g = min(g1, p1);
+    if (g >= g1) break;
+    ++it;
+    while (wk.prefix[it + 1] <= g) ++it;  // skip items without tiles
   }
-  if (p.lse != nullptr && dh == 0 && half == 0)
-    p.lse[orow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+}
+
+// One wave per (item, head): merge the pieces of items that span several
+// workgroups (LSE-weighted, as the combine step does), and write 0 / -inf for
+// items without tiles.  Items inside one workgroup's range are already final.
+__global__ __launch_bounds__(256) void decode_merge_kernel(const AttnParams p, const DecodeWork wk,
+                                                           int heads_per_group) {
+  using namespace dec;
+  const int lane = threadIdx.x % kWave;
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int items = p.num_tokens * p.num_splits;
+  if (row >= (int64_t)items * p.num_q_heads) return;
+  const int item = (int)(row / p.num_q_heads);
+  const int head = (int)(row - (int64_t)item * p.num_q_heads);
+  const int group = head / heads_per_group, hl = head - group * heads_per_group;
+  const int G = wk.grid;
+  const int total = wk.prefix[items];
+  const int per = max(1, (total + G - 1) / G);
+  const int p0 = wk.prefix[item], p1 = wk.prefix[item + 1];
+  const int token = item / p.num_splits, split = item - token * p.num_splits;
+  const int64_t orow = ((int64_t)split * p.num_tokens + token) * p.num_q_heads + head;
+  const int wf = p0 / per, wl = p1 > p0 ? (p1 - 1) / per : wf;
+  if (p1 > p0 && wf == wl) return;  // written by its workgroup
+
+  const int n = p1 > p0 ? wl - wf + 1 : 0;
+  auto piece_row = [&](int k) -> int64_t {
+    const int slot = k == 0 ? 2 * wf + 1 : 2 * (wf + k);
+    return ((int64_t)group * 2 * G + slot) * heads_per_group + hl;
+  };
+  float M = -INFINITY;
+  for (int k = lane; k < n; k += kWave) M = fmaxf(M, wk.piece_lse[piece_row(k)]);
+  M = wave_max(M);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    for (int base = 0; base < n; base += kWave) {
+      const int k = base + lane;
+      const float wt_lane = k < n ? __expf(wk.piece_lse[piece_row(k)] - M) : 0.f;
+      wsum += wave_sum(wt_lane);
+      const int cnt = min(kWave, n - base);
+      for (int j = 0; j < cnt; ++j) {
+        const float wt = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt_lane), j));
+        const float4* src =
+            reinterpret_cast<const float4*>(wk.piece_o + piece_row(base + j) * kDV + lane * 8);
+        const float4 a = src[0], b = src[1];
+        acc[0] += wt * a.x; acc[1] += wt * a.y; acc[2] += wt * a.z; acc[3] += wt * a.w;
+        acc[4] += wt * b.x; acc[5] += wt * b.y; acc[6] += wt * b.z; acc[7] += wt * b.w;
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  if (p.out_f32) {
+    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow * kDV + lane * 8);
+    dst[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    dst[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  } else {
+    *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(p.out) + orow * kDV + lane * 8) =
+        to_bf16x8(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv, acc[4] * inv,
+                  acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  }
+  if (p.lse != nullptr && lane == 0) p.lse[orow] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
 }
 
 bool decode_supported(const AttnParams& p) {
@@ -270,24 +567,94 @@ bool decode_supported(const AttnParams& p) {
          p.queries_per_kv % 32 == 0;
 }
 
-template <int NHB>
-static hipError_t launch_decode_t(const AttnParams& p, hipStream_t stream) {
-  const size_t lds = 2 * dec::kTileBytes + (size_t)(2 * NHB) * 16 * kWave * sizeof(float);
-  auto kern = decode_attention_kernel<NHB>;
+namespace {
+
+int heads_per_workgroup(const AttnParams& p) {
+  // as many query heads of one KV head per workgroup as the shapes allow
+  if (p.queries_per_kv % 128 == 0) return 128;
+  if (p.queries_per_kv % 64 == 0) return 64;
+  return 32;
+}
+
+// Workgroups per head group: one per CU (each holds a whole CU's LDS budget).
+int decode_grid(const AttnParams& p) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+  }
+  const int groups = p.num_q_heads / heads_per_workgroup(p);
+  return max(1, cus / max(1, groups));
+}
+
+constexpr int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+struct DecodeLayout {
+  int64_t prefix_off, lse_off, o_off, bytes;
+};
+
+DecodeLayout decode_layout(const AttnParams& p, int grid) {
+  const int64_t items = (int64_t)p.num_tokens * p.num_splits;
+  const int64_t pieces = (int64_t)2 * grid * p.num_q_heads;  // over all head groups
+  DecodeLayout l;
+  l.prefix_off = 0;
+  l.lse_off = align256((items + 1) * 4);
+  l.o_off = l.lse_off + align256(pieces * 4);
+  l.bytes = l.o_off + pieces * dec::kDV * 4;
+  return l;
+}
+
+template <int NB, int HG, bool UNIFORM_BT>
+hipError_t launch_decode_t(const AttnParams& p, const DecodeWork& wk, hipStream_t stream) {
+  constexpr int kBufs = UNIFORM_BT ? 3 : 2;
+  const size_t lds = kBufs * dec::kTileBytes + (size_t)(2 * HG) * NB * 16 * kWave * sizeof(float);
+  auto kern = decode_attention_kernel<NB, HG, UNIFORM_BT>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(p.num_tokens, p.num_q_heads / (NHB * 32), p.num_splits),
-                     dim3(NHB * 128), lds, stream, p);
+  hipLaunchKernelGGL(kern, dim3(wk.grid, p.num_q_heads / (HG * NB * 32)), dim3(HG * 128), lds,
+                     stream, p, wk);
   return hipGetLastError();
 }
 
-hipError_t launch_attention_decode(const AttnParams& p, hipStream_t stream) {
-  if (p.num_tokens == 0) return hipSuccess;
-  // as many 32-head blocks per workgroup as one KV head's query group allows
-  if (p.queries_per_kv % 128 == 0) return launch_decode_t<4>(p, stream);
-  if (p.queries_per_kv % 64 == 0) return launch_decode_t<2>(p, stream);
-  return launch_decode_t<1>(p, stream);
+template <bool UNIFORM_BT>
+hipError_t launch_decode_shape(const AttnParams& p, int heads, const DecodeWork& wk,
+                               hipStream_t stream) {
+  if (heads == 128) return launch_decode_t<DEC_NB, 4 / DEC_NB, UNIFORM_BT>(p, wk, stream);
+  if (heads == 64) return launch_decode_t<2, 1, UNIFORM_BT>(p, wk, stream);
+  return launch_decode_t<1, 1, UNIFORM_BT>(p, wk, stream);
+}
+
+}  // namespace
+
+int64_t decode_workspace_bytes(const AttnParams& p) {
+  return decode_layout(p, decode_grid(p)).bytes;
+}
+
+hipError_t launch_attention_decode(const AttnParams& p, void* workspace, hipStream_t stream) {
+  if (p.num_tokens == 0 || p.num_splits == 0) return hipSuccess;
+  const int grid = decode_grid(p);
+  const DecodeLayout l = decode_layout(p, grid);
+  char* ws = static_cast<char*>(workspace);
+  DecodeWork wk;
+  wk.prefix = reinterpret_cast<const int32_t*>(ws + l.prefix_off);
+  wk.piece_lse = reinterpret_cast<float*>(ws + l.lse_off);
+  wk.piece_o = reinterpret_cast<float*>(ws + l.o_off);
+  wk.grid = grid;
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(dec::kPlanThreads), 0, stream, p,
+                     reinterpret_cast<int32_t*>(ws + l.prefix_off));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int hpw = heads_per_workgroup(p);
+  // a 32-key tile lies inside one KV block when blocks hold at least 32 keys
+  if (p.block_size_log2 >= 5) e = launch_decode_shape<true>(p, hpw, wk, stream);
+  else e = launch_decode_shape<false>(p, hpw, wk, stream);
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)p.num_tokens * p.num_splits * p.num_q_heads;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+                     p, wk, hpw);
+  return hipGetLastError();
 }
 
 }  // namespace psw

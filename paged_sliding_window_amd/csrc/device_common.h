@@ -45,6 +45,32 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// 32-bit LDS address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
+}
+
+// The same transposed read issued as inline assembly.  With the builtin the
+// compiler cannot tell the read apart from LDS-DMA writes still in flight and
+// waits for every outstanding vector-memory load (vmcnt(0)) before it, which
+// stalls a loop that prefetches the next tiles with LDS-DMA.  The compiler does
+// not track this read: consume the result only after lds_wait_tr<N>(), which
+// waits until at most N LDS operations of this wave are outstanding (LDS
+// operations complete in issue order) and ties the registers to that wait.
+__device__ __forceinline__ bf16x4 lds_read_tr4_async(uint32_t addr) {
+  i16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait_tr(bf16x4& a, bf16x4& b) {
+  static_assert(N == 0 || N == 2 || N == 4, "lgkmcnt value");
+  if constexpr (N == 0) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
+  else if constexpr (N == 2) asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(a), "+v"(b));
+  else asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(a), "+v"(b));
+}
+
 __device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }

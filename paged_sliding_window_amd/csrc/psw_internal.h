@@ -57,6 +57,8 @@ bool prefill_supported(int head_dim_qk, int head_dim_v, int queries_per_kv, bool
 hipError_t launch_attention_prefill(const AttnParams& p, hipStream_t stream);
 
 bool decode_supported(const AttnParams& p);
-hipError_t launch_attention_decode(const AttnParams& p, hipStream_t stream);
+// Bytes of device workspace the latent decode needs on the current device.
+int64_t decode_workspace_bytes(const AttnParams& p);
+hipError_t launch_attention_decode(const AttnParams& p, void* workspace, hipStream_t stream);
 
 }  // namespace psw

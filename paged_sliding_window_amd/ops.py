@@ -103,9 +103,10 @@ def swa_mm_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[t
                      key_ranges: Optional[torch.Tensor] = None, head_dim_v: Optional[int] = None,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                      out_dtype: torch.dtype = torch.bfloat16, return_lse: bool = False,
-                     stream=None):
+                     workspace: Optional[torch.Tensor] = None, stream=None):
     """Paged attention; with key_ranges [S, num_seqs, 2] it writes S fp32/bf16
-    partials out[S, N, Hq, Dv] and lse[S, N, Hq]."""
+    partials out[S, N, Hq, Dv] and lse[S, N, Hq].  ``workspace`` (uint8, device)
+    is allocated here when the call needs one and none is given."""
     _need(q, "q", torch.bfloat16, 3)
     _need(k_cache, "k_cache", torch.bfloat16, 4)
     if v_cache is not None:
@@ -140,12 +141,25 @@ def swa_mm_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[t
                    chunk_lookback=chunk_lookback, mm_ranges=mm_ranges, key_ranges=key_ranges,
                    out=out, lse=lse, head_dim_v=head_dim_v, out_dtype=odt,
                    num_splits=num_splits)
+    need = attention_workspace_size(a)
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _need(workspace, "workspace", torch.uint8)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
     check(load().psw_swa_mm_attention(ctypes.byref(a), _stream(stream)))
     if key_ranges is None:
         out = out.view(n, hq, head_dim_v)
         if lse is not None:
             lse = lse.view(n, hq)
     return (out, lse) if (return_lse or num_splits > 1) else out
+
+
+def attention_workspace_size(args: PswAttnArgs) -> int:
+    """Bytes of workspace psw_swa_mm_attention needs for ``args`` (0: none)."""
+    n = ctypes.c_int64(0)
+    check(load().psw_attention_workspace_size(ctypes.byref(args), ctypes.byref(n)))
+    return n.value
 
 
 def lse_combine(partial_outs: Sequence[torch.Tensor], partial_lses: Sequence[torch.Tensor],

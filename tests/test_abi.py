@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     lib = psw.load()
-    assert lib.psw_abi_version() == 1
+    assert lib.psw_abi_version() == 2
     assert lib.psw_status_string(PSW_OK) == b"ok"
     assert lib.psw_status_string(PSW_ERR_INVALID) == b"invalid argument"
 
@@ -79,3 +79,42 @@ def test_other_entry_points_reject_bad_scalars():
     assert lib.psw_lse_combine(po, po, 65, 0, 1, 64, None, 0, None, None) == PSW_ERR_INVALID
     assert lib.psw_lse_combine(po, po, 1, 0, 1, 12, None, 0, None, None) == PSW_ERR_INVALID
     assert lib.psw_tile_bounds(ctypes.byref(_args()), 0, 16, 8, None, None, 0, None, None) == PSW_ERR_INVALID
+
+
+def _latent_decode_args(**kw):
+    return _args(num_seqs=4, num_tokens=4, num_q_heads=128, num_kv_heads=1, head_dim_qk=576,
+                 head_dim_v=512, block_size=64, **kw)
+
+
+def test_workspace_size_query():
+    lib = psw.load()
+    n = ctypes.c_int64(-1)
+    # separate K and V caches (prefill kernels): no workspace
+    assert lib.psw_attention_workspace_size(ctypes.byref(_args(num_seqs=1, num_tokens=8)),
+                                            ctypes.byref(n)) == PSW_OK
+    assert n.value == 0
+    # latent decode: prefix + pieces, growing with the number of (token, split) items
+    assert lib.psw_attention_workspace_size(ctypes.byref(_latent_decode_args()),
+                                            ctypes.byref(n)) == PSW_OK
+    one = n.value
+    assert one > 0 and one % 4 == 0
+    assert lib.psw_attention_workspace_size(
+        ctypes.byref(_latent_decode_args(num_splits=8, key_ranges=1)), ctypes.byref(n)) == PSW_OK
+    assert n.value >= one
+    assert lib.psw_attention_workspace_size(ctypes.byref(_args()), None) == PSW_ERR_INVALID
+
+
+def test_latent_decode_rejects_missing_or_small_workspace():
+    lib = psw.load()
+    fake = 0x100000  # never dereferenced: the call fails on the host
+    ptrs = dict(q=fake, k_cache=fake, block_table=fake, query_start_loc=fake, seq_lens=fake,
+                out=fake)
+    a = _latent_decode_args(**ptrs)
+    assert lib.psw_swa_mm_attention(ctypes.byref(a), None) == PSW_ERR_INVALID
+    assert b"workspace" in lib.psw_last_error()
+    n = ctypes.c_int64()
+    assert lib.psw_attention_workspace_size(ctypes.byref(a), ctypes.byref(n)) == PSW_OK
+    small = _latent_decode_args(workspace=fake, workspace_bytes=n.value - 1, **ptrs)
+    assert lib.psw_swa_mm_attention(ctypes.byref(small), None) == PSW_ERR_INVALID
+    misaligned = _latent_decode_args(workspace=fake + 16, workspace_bytes=n.value, **ptrs)
+    assert lib.psw_swa_mm_attention(ctypes.byref(misaligned), None) == PSW_ERR_INVALID

@@ -91,3 +91,60 @@ def test_lse_combine_random_partials(P, pdt, odt):
     ref_o, ref_l = lse_merge_ref(ref_in, lses)
     assert_close(out.float().cpu().numpy(), ref_o, "combine out")
     assert_lse_close(ol.cpu().numpy(), ref_l, "combine lse")
+
+
+def _keep_last_tokens(w, k):
+    """Keep the last (up to) k new tokens of every request: a decode step with
+    several new tokens per request (the earlier ones become cached context)."""
+    keep, qls = [], []
+    for r in range(w.num_seqs):
+        t0, t1 = int(w.query_start_loc[r]), int(w.query_start_loc[r + 1])
+        n = min(k, t1 - t0)
+        keep.extend(range(t1 - n, t1))
+        qls.append(n)
+    keep = np.array(keep)
+    w.q_bits = w.q_bits[keep]
+    w.positions = w.positions[keep]
+    w.query_lens = np.array(qls, dtype=np.int64)
+    w.context_lens = w.seq_lens - w.query_lens
+    w.query_start_loc = np.concatenate([[0], np.cumsum(qls)]).astype(np.int32)
+    return w
+
+
+# Latent decode under the balanced (stream-K) schedule: blocks of 16 keys (a tile
+# spans two blocks), 32 / 64 / 128 heads per KV head, sliding windows and image
+# ranges (splits that the mask empties), several new tokens per request, and
+# more than 1,024 (token, split) items.
+@pytest.mark.parametrize("case", [
+    dict(seed=951, num_seqs=6, max_len=1500, hq=128, block_size=16, window=100, max_ranges=3,
+         splits=4, tokens=3),
+    dict(seed=952, num_seqs=4, max_len=2500, hq=64, block_size=64, window=0, max_ranges=0,
+         splits=3, tokens=2),
+    dict(seed=953, num_seqs=5, max_len=900, hq=32, block_size=32, window=33, max_ranges=2,
+         splits=2, tokens=4),
+    dict(seed=954, num_seqs=64, max_len=400, hq=32, block_size=64, window=0, max_ranges=0,
+         splits=8, tokens=3),
+], ids=["bs16_window_images", "qpk64", "qpk32_window", "over_1024_items"])
+def test_latent_decode_scheduling(case):
+    from workloads.synth import decode_split_ranges
+    c = dict(case)
+    splits, tokens = c.pop("splits"), c.pop("tokens")
+    w = make_small_case(c.pop("seed"), hkv=1, d=576, dv=512, causal=True, chunk=(0, -1),
+                        latent=True, **c)
+    w = _keep_last_tokens(w, tokens)
+    w.key_ranges = decode_split_ranges(w.seq_lens, splits)
+    w.current_ranges = np.stack([np.stack([w.seq_lens - 1, w.seq_lens], 1)]).astype(np.int32)
+    if case["seed"] == 954:
+        assert w.num_tokens * splits > 1024
+    gw = GpuWorkload(w)
+    out, lse, hist_o, hist_l, cur_o, cur_l = _decode(gw, w)
+    out = out.float().cpu().numpy().reshape(w.num_tokens, w.num_q_heads, w.head_dim_v)
+    ho, hl = hist_o.cpu().numpy(), hist_l.cpu().numpy()
+    for r in range(w.num_seqs):
+        t0, t1 = w.query_start_loc[r], w.query_start_loc[r + 1]
+        ref_o, _ = oracle_rows(w, r)
+        assert_close(out[t0:t1], ref_o, f"merged, request {r}")
+        for j in range(splits):
+            ref_o, ref_l = oracle_rows(w, r, key_range=tuple(w.key_ranges[j, r]))
+            assert_close(ho[j, t0:t1], ref_o, f"split {j} of request {r}")
+            assert_lse_close(hl[j, t0:t1], ref_l, f"split {j} of request {r} lse")
