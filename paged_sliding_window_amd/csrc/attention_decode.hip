@@ -165,23 +165,6 @@ struct DecodeWork {
   int grid;               // workgroups per head group
 };
 
-// Workgroup barrier for LDS data: this wave's LDS reads and writes retire
-// (lgkmcnt) before the barrier, and the memory clobber keeps the compiler from
-// moving memory accesses across it.  Unlike __syncthreads() it does not wait
-// for vector-memory operations, so LDS-DMA tile prefetches stay in flight; a
-// tile's own DMA is waited for with an explicit vmcnt before the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (expcnt and lgkmcnt left alone).
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
-__device__ __forceinline__ int load_uniform_i32(const int32_t* ptr) {
-  return *(const __attribute__((address_space(4))) int32_t*)ptr;
-}
-
 // NB: 32-head MFMA blocks per wave; HG: head groups per workgroup.  The
 // workgroup has 2 * HG waves, wave (hg, dh) owns heads [hg * NB * 32, +NB * 32)
 // of the group and the d-half dh; one wave per SIMD, so each wave has the whole

@@ -84,7 +84,8 @@ prefill_attention_kernel(const AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
-  const int lane = tid % kWave, wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: keep it scalar
   const int half = lane >> 5;
   const int qpk = p.queries_per_kv;
   const int block_q = S::kBlockM / qpk;
@@ -171,27 +172,45 @@ prefill_attention_kernel(const AttnParams p) {
     const int bs_mask = (1 << bs_log2) - 1;
     const float c2 = p.scale_log2;
 
-    // Lane l holds the physical block of key (tile * 64 + l) of the next tile;
-    // keys past the end are clamped to the last key (finite data, masked out).
+    // LDS-DMA instruction g moves rows g + kInstrPerTile * q, q = lane / (D / 8),
+    // 16-byte chunk lane % (D / 8) of each, into the block at g * k/vBlock.  A
+    // wave issues instructions g = wave * kInstrPerWave + i, so a lane's rows in
+    // a tile are the consecutive keys r0 + i: when blocks hold at least
+    // kInstrPerWave keys they share one block, whose table entry the lane
+    // prefetches (fetch_block) and whose addresses differ by one slot pitch.
+    const int dma_q = lane / (D / 8), dma_ch = lane % (D / 8);
+    const int r0 = wave * S::kInstrPerWave + S::kInstrPerTile * dma_q;
+    const bool group_in_block = (1 << bs_log2) >= S::kInstrPerWave;
+    // block of this lane's first row in the tile (clamped to the last key)
     auto fetch_block = [&](int tile) -> int {
-      const int key = min(tile * S::kTile + lane, seq_len - 1);
+      const int key = min(tile * S::kTile + r0, seq_len - 1);
       return bt[key >> bs_log2];
     };
-    // LDS-DMA instruction g moves rows g + kInstrPerTile * q, q = lane / (D / 8),
-    // 16-byte chunk lane % (D / 8) of each, into the block at g * k/vBlock.
-    const int dma_q = lane / (D / 8), dma_ch = lane % (D / 8);
     auto issue_tile = [&](int tile, int buf, int blk_of_lane) {
       char* kt = smem + buf * (S::kKBytes + S::kVBytes);
       char* vt = kt + S::kKBytes;
+      const int first = tile * S::kTile;
+      if (group_in_block && first + S::kTile <= seq_len) {
+        const int64_t cache_row = ((int64_t)blk_of_lane << bs_log2) + ((first + r0) & bs_mask);
+        const uint16_t* ks = kbase + cache_row * k_slot_pitch + dma_ch * 8;
+        const uint16_t* vs = vbase + cache_row * v_slot_pitch + dma_ch * 8;
 #pragma unroll
-      for (int i = 0; i < S::kInstrPerWave; ++i) {
-        const int g = wave * S::kInstrPerWave + i;
-        const int row = g + S::kInstrPerTile * dma_q;
-        const int key = min(tile * S::kTile + row, seq_len - 1);
-        const int blk = __shfl(blk_of_lane, row, kWave);
-        const int64_t cache_row = ((int64_t)blk << bs_log2) + (key & bs_mask);
-        lds_dma16(kbase + cache_row * k_slot_pitch + dma_ch * 8, kt + g * S::kKBlock);
-        lds_dma16(vbase + cache_row * v_slot_pitch + dma_ch * 8, vt + g * S::kVBlock);
+        for (int i = 0; i < S::kInstrPerWave; ++i) {
+          const int g = wave * S::kInstrPerWave + i;
+          lds_dma16(ks + i * k_slot_pitch, kt + g * S::kKBlock);
+          lds_dma16(vs + i * v_slot_pitch, vt + g * S::kVBlock);
+        }
+      } else {
+        // last tile (rows past the end repeat the last key: finite data, masked
+        // out) or blocks smaller than a lane's row group: one lookup per row
+#pragma unroll
+        for (int i = 0; i < S::kInstrPerWave; ++i) {
+          const int g = wave * S::kInstrPerWave + i;
+          const int key = min(first + r0 + i, seq_len - 1);
+          const int64_t cache_row = ((int64_t)bt[key >> bs_log2] << bs_log2) + (key & bs_mask);
+          lds_dma16(kbase + cache_row * k_slot_pitch + dma_ch * 8, kt + g * S::kKBlock);
+          lds_dma16(vbase + cache_row * v_slot_pitch + dma_ch * 8, vt + g * S::kVBlock);
+        }
       }
     };
 
@@ -259,17 +278,35 @@ prefill_attention_kernel(const AttnParams p) {
         l_run += psum;
         const bf16x8 pf0 = to_bf16x8(s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]);
         const bf16x8 pf1 = to_bf16x8(s[8], s[9], s[10], s[11], s[12], s[13], s[14], s[15]);
-#pragma unroll
-        for (int b = 0; b < S::kOBlocks; ++b) {
-          const int col = b * 32 + tr_col;  // bf16 column
+        // O^T += V^T P^T, output columns b*32 + [0, 32), keys kb*32 + 16 j + [0, 16)
+        // in step st = 2b + j.  The transposed reads of step st + 1 are issued
+        // before the MFMA of step st (and, unlike the builtin, do not make the
+        // compiler wait for the prefetch of tile t + 1 still in flight).
+        {
+          const uint32_t vcol = lds_addr(vt + tr_col * 2);
+          uint32_t va[2][2];
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            const int ra = kb * 32 + 16 * j + tr_row, rb = ra + 8;
-            const bf16x4 lo = lds_read_tr4(reinterpret_cast<const __bf16*>(
-                vt + lds_row<S>(ra, S::kVBlock) + col * 2));
-            const bf16x4 hi = lds_read_tr4(reinterpret_cast<const __bf16*>(
-                vt + lds_row<S>(rb, S::kVBlock) + col * 2));
-            o[b] = mfma32(cat8(lo, hi), j == 0 ? pf0 : pf1, o[b]);
+            const int ra = kb * 32 + 16 * j + tr_row;
+            va[j][0] = vcol + lds_row<S>(ra, S::kVBlock);
+            va[j][1] = vcol + lds_row<S>(ra + 8, S::kVBlock);
+          }
+          constexpr int kSteps = 2 * S::kOBlocks;
+          bf16x4 vr[2][2];
+          vr[0][0] = lds_read_tr4_async(va[0][0]);
+          vr[0][1] = lds_read_tr4_async(va[0][1]);
+#pragma unroll
+          for (int st = 0; st < kSteps; ++st) {
+            const int b = st >> 1, j = st & 1, cur = st & 1;
+            if (st + 1 < kSteps) {
+              const int bn = (st + 1) >> 1, jn = (st + 1) & 1;
+              vr[cur ^ 1][0] = lds_read_tr4_async(va[jn][0] + bn * 64);
+              vr[cur ^ 1][1] = lds_read_tr4_async(va[jn][1] + bn * 64);
+              lds_wait_tr<2>(vr[cur][0], vr[cur][1]);
+            } else {
+              lds_wait_tr<0>(vr[cur][0], vr[cur][1]);
+            }
+            o[b] = mfma32(cat8(vr[cur][0], vr[cur][1]), j == 0 ? pf0 : pf1, o[b]);
           }
         }
       }

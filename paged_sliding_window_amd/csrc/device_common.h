@@ -100,6 +100,23 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Workgroup barrier for LDS data: this wave's LDS reads and writes retire
+// (lgkmcnt) before the barrier, and the memory clobber keeps the compiler from
+// moving memory accesses across it.  Unlike __syncthreads() it does not wait
+// for vector-memory operations, so LDS-DMA tile prefetches stay in flight; a
+// tile's own DMA is waited for with an explicit vmcnt before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left alone).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+__device__ __forceinline__ int load_uniform_i32(const int32_t* ptr) {
+  return *(const __attribute__((address_space(4))) int32_t*)ptr;
+}
+
 // Workgroups are handed to the 8 XCDs round-robin by linear id (id % 8), and
 // each XCD has its own L2.  This bijection gives XCD x the contiguous range of
 // logical ids [x * q + min(x, r), ...) (q = n / 8, r = n % 8), so neighbouring
