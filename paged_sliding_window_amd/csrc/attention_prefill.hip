@@ -9,65 +9,74 @@
 //     shares it (GQA).  Workgroups are ordered so each XCD walks consecutive
 //     query blocks of one KV head (their K/V windows overlap);
 //   * two workgroups share a CU, so each SIMD runs two waves whose tile
-//     barriers are independent: one wave's softmax overlaps the other's MFMAs
-//     (a single 8-wave workgroup keeps both waves of a SIMD in the same phase);
+//     barriers are independent.  A SIMD overlaps one wave's vector ALU work
+//     (softmax) with the other wave's MFMAs, while inside one wave the two
+//     serialise: the kernel keeps the vector instruction count per MFMA low;
 //   * KV tiles of 32 keys are gathered from the paged cache through the block
 //     table with direct-to-LDS 16-byte loads (global_load_lds_dwordx4), double
-//     buffered (68 KB per workgroup at head dim 256): the loads of tile t+1 and
-//     the block-table reads of tile t+2 are in flight while tile t is computed.  Each load instruction writes whole
-//     rows as one block and blocks are padded (K by 16 bytes, V by 64), so the
-//     K reads below and the transposed V reads hit distinct banks while every
-//     LDS address stays a lane base plus an immediate;
+//     buffered: the loads of tile t+1 are in flight while tile t is computed.
+//     The block-table entries of a tile are read with scalar loads one tile
+//     ahead, and a load's address is a scalar base (block, row group) plus a
+//     32-bit per-lane offset, so issuing a tile costs a few vector
+//     instructions.  Each load instruction writes whole rows as one block and
+//     blocks are padded (K by 16 bytes, V by 64), so the K reads and the
+//     transposed V reads hit distinct banks while every LDS address is a lane
+//     base plus an immediate;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K from LDS as the A operand, Q
-//     held in registers as the B operand, so each lane ends up holding 32 scores
-//     of ONE query row (the row's other 32 keys sit in lane ^ 32) and the online
+//     held in registers as the B operand, so each lane holds 16 scores of ONE
+//     query row (the row's other 16 keys sit in lane ^ 32) and the online
 //     softmax needs a single cross-half exchange per tile;
 //   * O^T += V^T P^T: P^T comes straight from the S^T accumulators (rounded to
 //     bf16), V^T is read out of the row-major V tile with ds_read_b64_tr_b16, and
-//     O^T keeps one query row per lane, so rescaling is per lane;
+//     O^T keeps one query row per lane, so rescaling is per lane.  The row sum
+//     is taken over the same bf16 probabilities with v_dot2 (two per
+//     instruction).  LDS reads run a few ahead of their MFMAs with explicit
+//     waits;
 //   * the running max is only moved when a tile's max exceeds it by more than
 //     2^8 (log2 units); otherwise P may reach 256, still exact in bf16/fp32, and
 //     the O rescale is skipped for the whole wave;
-//   * per-element masking only on tiles not entirely inside every row's allowed
-//     interval (each row's allowed keys form one interval).
+//   * a wave skips tiles outside the union of its rows' allowed intervals, and
+//     masks per element only tiles not inside every row's interval (each row's
+//     allowed keys form one interval).
+#include <utility>
+
 #include "device_common.h"
 #include "psw_internal.h"
 
 namespace psw {
 
-template <int D, int DV>
+template <int D>
 struct PrefillShape {
   static constexpr int kWaves = 4;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kRowsPerWave = 32;
   static constexpr int kBlockM = kWaves * kRowsPerWave;
   static constexpr int kTile = 32;
-  static constexpr int kKChunks = D / 8;   // 16-byte chunks per K row
-  static constexpr int kVChunks = DV / 8;
   // LDS layout of a tile: one LDS-DMA instruction moves 1 KB = kRowsPerInstr
   // whole rows (rows g, g + kInstrPerTile, ...), written as one block; blocks
   // are kKBlock / kVBlock bytes apart.  The 16 extra bytes per K block put 16
   // consecutive rows read at the same column in 16 distinct bank groups; the
   // 64 extra bytes per V block do the same for the 4 rows x 4 chunks of a
-  // transposed read.  Every LDS address is a per-lane base plus immediates.
+  // transposed read.
   static constexpr int kRowsPerInstr = 1024 / (D * 2);
   static constexpr int kInstrPerTile = kTile / kRowsPerInstr;
   static constexpr int kInstrPerWave = kInstrPerTile / kWaves;
   static constexpr int kKBlock = 1024 + 16;
   static constexpr int kVBlock = 1024 + 64;
-  static constexpr int kQFrags = D / 16;
-  static constexpr int kOBlocks = DV / 32;
   static constexpr int kKBytes = kInstrPerTile * kKBlock;
   static constexpr int kVBytes = kInstrPerTile * kVBlock;
-  static_assert(D == DV, "K and V tiles share the row-to-instruction mapping");
+  static constexpr int kBufBytes = kKBytes + kVBytes;
+  static constexpr int kQFrags = D / 16;   // MFMA k-steps of the score product
+  static constexpr int kOBlocks = D / 32;  // 32-column output blocks
+  static constexpr int kPvSteps = 2 * kOBlocks;
   static_assert(kRowsPerInstr * D * 2 == 1024 && kInstrPerWave * kWaves == kInstrPerTile,
                 "tile rows must split evenly into LDS-DMA instructions and waves");
-  static_assert(2 * (kKBytes + kVBytes) <= 160 * 1024, "double buffer exceeds LDS");
+  static_assert(2 * kBufBytes <= 80 * 1024, "two workgroups must fit in one CU's LDS");
 };
 
 // Byte offset of tile row r inside a K or V tile buffer.
 template <class S>
-__device__ __forceinline__ int lds_row(int r, int block_bytes) {
+__host__ __device__ constexpr int lds_row(int r, int block_bytes) {
   return (r % S::kInstrPerTile) * block_bytes + (r / S::kInstrPerTile) * (1024 / S::kRowsPerInstr);
 }
 
@@ -77,10 +86,50 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_dst) {
       (__attribute__((address_space(3))) void*)(lds_void*)lds_dst, 16, 0, 0);
 }
 
-template <int D, int DV>
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// LDS reads the compiler does not track (see lds_read_tr4_async): the result
+// may be consumed only after lds_wait<N>() on it.
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_read_b128_at(uint32_t addr) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ bf16x4 lds_read_tr4_at(uint32_t addr) {
+  i16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return __builtin_bit_cast(bf16x4, r);
+}
+// Wait until at most N LDS operations of this wave are outstanding (they
+// complete in issue order; outstanding scalar loads only make the wait longer)
+// and tie the given registers to that point.
+template <int N>
+__device__ __forceinline__ void lds_wait(bf16x8& a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N < 15 ? N : 15));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(bf16x4& a, bf16x4& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N < 15 ? N : 15));
+}
+
+__device__ __forceinline__ float dot2_bf16(bf16x2 a, bf16x2 b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void
 prefill_attention_kernel(const AttnParams p) {
-  using S = PrefillShape<D, DV>;
+  using S = PrefillShape<D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
@@ -139,12 +188,20 @@ prefill_attention_kernel(const AttnParams p) {
       row_hi = (int)hi64;
     }
   }
-  // the wave's common interval: 32-key halves inside it need no per-element mask
+  // The wave's common interval (tiles inside it need no per-element mask) and
+  // the union of its rows' intervals (tiles outside it are skipped).
   int wave_lo = row_valid ? row_lo : INT32_MIN, wave_hi = row_valid ? row_hi : INT32_MAX;
+  int any_lo = row_lo, any_hi = row_hi;
   for (int o = 32; o > 0; o >>= 1) {
     wave_lo = max(wave_lo, __shfl_xor(wave_lo, o, kWave));
     wave_hi = min(wave_hi, __shfl_xor(wave_hi, o, kWave));
+    any_lo = min(any_lo, __shfl_xor(any_lo, o, kWave));
+    any_hi = max(any_hi, __shfl_xor(any_hi, o, kWave));
   }
+  wave_lo = __builtin_amdgcn_readfirstlane(wave_lo);
+  wave_hi = __builtin_amdgcn_readfirstlane(wave_hi);
+  any_lo = __builtin_amdgcn_readfirstlane(any_lo);
+  any_hi = __builtin_amdgcn_readfirstlane(any_hi);
 
   bf16x8 qf[S::kQFrags];
   {
@@ -162,153 +219,178 @@ prefill_attention_kernel(const AttnParams p) {
   float m_run = -INFINITY, l_run = 0.f;
 
   if (t_lo < t_hi) {
-    const bool latent = p.v_cache == p.k_cache;
-    const int64_t k_slot_pitch = (int64_t)p.num_kv_heads * D;
-    const int64_t v_slot_pitch = latent ? k_slot_pitch : (int64_t)p.num_kv_heads * DV;
-    const uint16_t* kbase = p.k_cache + (int64_t)kvh * D;
-    const uint16_t* vbase = p.v_cache + (int64_t)kvh * (latent ? D : DV);
+    // K and V rows have the same pitch (head_dim_qk == head_dim_v here)
+    const int64_t pitch = (int64_t)p.num_kv_heads * D * 2;  // bytes per cache slot
+    const char* kbase = reinterpret_cast<const char*>(p.k_cache + (int64_t)kvh * D);
+    const char* vbase = reinterpret_cast<const char*>(p.v_cache + (int64_t)kvh * D);
     const int32_t* bt = p.block_table + (int64_t)seq * p.block_table_stride;
     const int bs_log2 = p.block_size_log2;
     const int bs_mask = (1 << bs_log2) - 1;
     const float c2 = p.scale_log2;
 
     // LDS-DMA instruction g moves rows g + kInstrPerTile * q, q = lane / (D / 8),
-    // 16-byte chunk lane % (D / 8) of each, into the block at g * k/vBlock.  A
-    // wave issues instructions g = wave * kInstrPerWave + i, so a lane's rows in
-    // a tile are the consecutive keys r0 + i: when blocks hold at least
-    // kInstrPerWave keys they share one block, whose table entry the lane
-    // prefetches (fetch_block) and whose addresses differ by one slot pitch.
+    // 16-byte chunk lane % (D / 8) of each.  Wave w issues g = w * kInstrPerWave
+    // + i.  With blocks of >= 16 keys the 32 keys of a tile lie in one or two
+    // blocks: keys [first, first + 16) in block b0 and the rest in b1 (the same
+    // block for larger blocks), so lane row g + rq, rq = kInstrPerTile * q,
+    // sits at seg(sel) + g * pitch + lane_off, with sel = (rq >= 16) when blocks
+    // hold 16 keys and lane_off = (rq within its segment) * pitch + chunk * 16.
     const int dma_q = lane / (D / 8), dma_ch = lane % (D / 8);
-    const int r0 = wave * S::kInstrPerWave + S::kInstrPerTile * dma_q;
-    const bool group_in_block = (1 << bs_log2) >= S::kInstrPerWave;
-    // block of this lane's first row in the tile (clamped to the last key)
-    auto fetch_block = [&](int tile) -> int {
-      const int key = min(tile * S::kTile + r0, seq_len - 1);
-      return bt[key >> bs_log2];
+    const int rq = S::kInstrPerTile * dma_q;
+    const bool fast_blocks = bs_log2 >= 4;
+    const bool two_segs = bs_log2 == 4;
+    const bool lane_second = two_segs && rq >= 16;
+    const uint32_t lane_off = (uint32_t)(((two_segs ? (rq & 15) : rq) * pitch) + dma_ch * 16);
+
+    // scalar block-table reads of a tile: the blocks of keys first and first + 16
+    auto tile_blocks = [&](int tile, int& b0, int& b1) __attribute__((always_inline)) {
+      const int first = tile * S::kTile;
+      b0 = load_uniform_i32(bt + (first >> bs_log2));
+      b1 = b0;
+      if (two_segs && first + 16 < seq_len) b1 = load_uniform_i32(bt + ((first + 16) >> bs_log2));
     };
-    auto issue_tile = [&](int tile, int buf, int blk_of_lane) {
-      char* kt = smem + buf * (S::kKBytes + S::kVBytes);
+    auto issue_tile = [&](int tile, int buf, int b0, int b1) __attribute__((always_inline)) {
+      char* kt = smem + buf * S::kBufBytes;
       char* vt = kt + S::kKBytes;
       const int first = tile * S::kTile;
-      if (group_in_block && first + S::kTile <= seq_len) {
-        const int64_t cache_row = ((int64_t)blk_of_lane << bs_log2) + ((first + r0) & bs_mask);
-        const uint16_t* ks = kbase + cache_row * k_slot_pitch + dma_ch * 8;
-        const uint16_t* vs = vbase + cache_row * v_slot_pitch + dma_ch * 8;
+      // byte offsets of the two segments in the cache (first row of each)
+      const int64_t seg0 = (((int64_t)b0 << bs_log2) + (first & bs_mask)) * pitch;
+      const int64_t seg1 = ((int64_t)b1 << bs_log2) * pitch;
+      const int64_t lo = two_segs ? min(seg0, seg1) : seg0;
+      const int64_t delta = two_segs ? max(seg0, seg1) - lo : 0;
+      if (fast_blocks && first + S::kTile <= seq_len && delta < ((int64_t)1 << 31)) {
+        // scalar base + one 32-bit offset per lane for every instruction
+        const bool lane_far = lane_second ? seg1 > seg0 : seg0 > seg1;
+        const uint32_t voff = lane_off + (lane_far ? (uint32_t)delta : 0u);
 #pragma unroll
         for (int i = 0; i < S::kInstrPerWave; ++i) {
           const int g = wave * S::kInstrPerWave + i;
-          lds_dma16(ks + i * k_slot_pitch, kt + g * S::kKBlock);
-          lds_dma16(vs + i * v_slot_pitch, vt + g * S::kVBlock);
+          const int64_t row = lo + g * pitch;
+          lds_dma16(kbase + row + voff, kt + g * S::kKBlock);
+          lds_dma16(vbase + row + voff, vt + g * S::kVBlock);
         }
       } else {
-        // last tile (rows past the end repeat the last key: finite data, masked
-        // out) or blocks smaller than a lane's row group: one lookup per row
+        // last tile (rows past the end repeat the last key: finite data,
+        // masked out), blocks below 16 keys, or segments far apart: per-lane
+        // 64-bit addresses and table reads
 #pragma unroll
         for (int i = 0; i < S::kInstrPerWave; ++i) {
           const int g = wave * S::kInstrPerWave + i;
-          const int key = min(first + r0 + i, seq_len - 1);
-          const int64_t cache_row = ((int64_t)bt[key >> bs_log2] << bs_log2) + (key & bs_mask);
-          lds_dma16(kbase + cache_row * k_slot_pitch + dma_ch * 8, kt + g * S::kKBlock);
-          lds_dma16(vbase + cache_row * v_slot_pitch + dma_ch * 8, vt + g * S::kVBlock);
+          const int key = min(first + g + rq, seq_len - 1);
+          const int64_t row = (((int64_t)bt[key >> bs_log2] << bs_log2) + (key & bs_mask)) * pitch +
+                              dma_ch * 16;
+          lds_dma16(kbase + row, kt + g * S::kKBlock);
+          lds_dma16(vbase + row, vt + g * S::kVBlock);
         }
       }
     };
-
-    int blk_next = fetch_block(t_lo);
-    issue_tile(t_lo, 0, blk_next);
-    if (t_lo + 1 < t_hi) blk_next = fetch_block(t_lo + 1);
 
     const int tr_row = half * 4 + ((lane & 15) >> 2);
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // bf16 column in a 32-block
+    const uint32_t k_lane = (uint32_t)(lds_row<S>(lane & 31, S::kKBlock) + half * 16);
+    const uint32_t v_lane = (uint32_t)(S::kKBytes + tr_col * 2);
+    uint32_t v_rows[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      v_rows[j][0] = v_lane + (uint32_t)lds_row<S>(16 * j + tr_row, S::kVBlock);
+      v_rows[j][1] = v_lane + (uint32_t)lds_row<S>(16 * j + tr_row + 8, S::kVBlock);
+    }
+    const uint32_t smem0 = lds_addr(smem);
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+    int nb0, nb1;
+    tile_blocks(t_lo, nb0, nb1);
+    issue_tile(t_lo, 0, nb0, nb1);
+    if (t_lo + 1 < t_hi) tile_blocks(t_lo + 1, nb0, nb1);
 
     for (int t = t_lo; t < t_hi; ++t) {
       const int buf = (t - t_lo) & 1;
-      // this wave's LDS-DMA loads of tile t and its block-table read have
-      // landed; the barrier extends that to every wave and fences the reads of
-      // the other buffer (tile t-1) before it is refilled
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      // this wave's LDS-DMA loads of tile t have landed; the barrier extends
+      // that to every wave and fences the reads of the other buffer (tile t-1)
+      // before it is refilled
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      lds_barrier();
       if (t + 1 < t_hi) {
-        issue_tile(t + 1, buf ^ 1, blk_next);
-        if (t + 2 < t_hi) blk_next = fetch_block(t + 2);
+        issue_tile(t + 1, buf ^ 1, nb0, nb1);
+        if (t + 2 < t_hi) tile_blocks(t + 2, nb0, nb1);
       }
-      const char* kt = smem + buf * (S::kKBytes + S::kVBytes);
-      const char* vt = kt + S::kKBytes;
+      const int base = t * S::kTile;
+      if (base > any_hi || base + S::kTile - 1 < any_lo) continue;  // no row of the wave sees it
+      const uint32_t kt = smem0 + (uint32_t)(buf * S::kBufBytes);
 
-#pragma unroll
-      for (int kb = 0; kb < S::kTile / 32; ++kb) {
-        const int base = t * S::kTile + kb * 32;
-        // S^T[key][row] for 32 keys
-        f32x16 s = f32x16{};
-        const int kr = kb * 32 + (lane & 31);
-#pragma unroll
-        for (int c = 0; c < S::kQFrags; ++c) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              kt + lds_row<S>(kr, S::kKBlock) + (2 * c + half) * 16);
-          s = mfma32(a, qf[c], s);
-        }
-        if (!(base >= wave_lo && base + 31 <= wave_hi)) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int k = base + (i / 4) * 8 + half * 4 + (i % 4);
-            s[i] = (k >= row_lo && k <= row_hi) ? s[i] : -INFINITY;
-          }
-        }
-        float mx = s[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-        mx = fmaxf(mx, swap_halves(mx)) * c2;
-        // move the running max only when it grows by more than 2^8
-        if (__ballot(mx > m_run + 8.f) != 0) {
-          const float m_new = fmaxf(m_run, mx);
-          // 0 when only m_run is -inf; 1 for a row that is still fully masked
-          const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
-          l_run *= alpha;
-#pragma unroll
-          for (int b = 0; b < S::kOBlocks; ++b) o[b] *= alpha;
-          m_run = m_new;
-        }
-        const float m_sub = m_run == -INFINITY ? 0.f : m_run;
-        float psum = 0.f;
+      // S^T[key][row] for the 32 keys; K k-chunks read KA ahead
+      f32x16 s;
+      {
+        constexpr int N = S::kQFrags, KA = 3;
+        const uint32_t ka = kt + k_lane;
+        bf16x8 kf[KA + 1];
+        static_for<KA>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          kf[c] = lds_read_b128_at<c * 32>(ka);
+        });
+        s = f32x16{};
+        static_for<N>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          constexpr int issued = c + KA < N ? c + KA : N;
+          lds_wait<issued - 1 - c>(kf[c % (KA + 1)]);
+          s = mfma32(kf[c % (KA + 1)], qf[c], s);
+          if constexpr (c + KA < N) kf[(c + KA) % (KA + 1)] = lds_read_b128_at<(c + KA) * 32>(ka);
+        });
+      }
+      if (!(base >= wave_lo && base + S::kTile - 1 <= wave_hi)) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          s[i] = fast_exp2(fmaf(s[i], c2, -m_sub));
-          psum += s[i];
+          const int k = base + (i / 4) * 8 + half * 4 + (i % 4);
+          s[i] = (k >= row_lo && k <= row_hi) ? s[i] : -INFINITY;
         }
-        l_run += psum;
-        const bf16x8 pf0 = to_bf16x8(s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]);
-        const bf16x8 pf1 = to_bf16x8(s[8], s[9], s[10], s[11], s[12], s[13], s[14], s[15]);
-        // O^T += V^T P^T, output columns b*32 + [0, 32), keys kb*32 + 16 j + [0, 16)
-        // in step st = 2b + j.  The transposed reads of step st + 1 are issued
-        // before the MFMA of step st (and, unlike the builtin, do not make the
-        // compiler wait for the prefetch of tile t + 1 still in flight).
-        {
-          const uint32_t vcol = lds_addr(vt + tr_col * 2);
-          uint32_t va[2][2];
+      }
+      float mx = s[0];
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int ra = kb * 32 + 16 * j + tr_row;
-            va[j][0] = vcol + lds_row<S>(ra, S::kVBlock);
-            va[j][1] = vcol + lds_row<S>(ra + 8, S::kVBlock);
-          }
-          constexpr int kSteps = 2 * S::kOBlocks;
-          bf16x4 vr[2][2];
-          vr[0][0] = lds_read_tr4_async(va[0][0]);
-          vr[0][1] = lds_read_tr4_async(va[0][1]);
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+      mx = fmaxf(mx, swap_halves(mx)) * c2;
+      // move the running max only when it grows by more than 2^8
+      if (__ballot(mx > m_run + 8.f) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        // 0 when only m_run is -inf; 1 for a row that is still fully masked
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-          for (int st = 0; st < kSteps; ++st) {
-            const int b = st >> 1, j = st & 1, cur = st & 1;
-            if (st + 1 < kSteps) {
-              const int bn = (st + 1) >> 1, jn = (st + 1) & 1;
-              vr[cur ^ 1][0] = lds_read_tr4_async(va[jn][0] + bn * 64);
-              vr[cur ^ 1][1] = lds_read_tr4_async(va[jn][1] + bn * 64);
-              lds_wait_tr<2>(vr[cur][0], vr[cur][1]);
-            } else {
-              lds_wait_tr<0>(vr[cur][0], vr[cur][1]);
-            }
-            o[b] = mfma32(cat8(vr[cur][0], vr[cur][1]), j == 0 ? pf0 : pf1, o[b]);
-          }
-        }
+        for (int b = 0; b < S::kOBlocks; ++b) o[b] *= alpha;
+        m_run = m_new;
+      }
+      const float m_sub = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = fast_exp2(fmaf(s[i], c2, -m_sub));
+      const bf16x8 pf0 = to_bf16x8(s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]);
+      const bf16x8 pf1 = to_bf16x8(s[8], s[9], s[10], s[11], s[12], s[13], s[14], s[15]);
+      // row sum over the bf16 probabilities the output product uses
+      static_for<4>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        l_run = dot2_bf16(__builtin_shufflevector(pf0, pf0, 2 * i, 2 * i + 1), ones, l_run);
+        l_run = dot2_bf16(__builtin_shufflevector(pf1, pf1, 2 * i, 2 * i + 1), ones, l_run);
+      });
+
+      // O^T += V^T P^T: step st covers output columns b*32 + [0, 32) and keys
+      // 16 j + [0, 16), j = st / kOBlocks, b = st % kOBlocks; the transposed
+      // reads run VA steps ahead
+      {
+        constexpr int N = S::kPvSteps, VA = 2;
+        bf16x4 vr[VA + 1][2];
+        auto read_v = [&](auto ss) __attribute__((always_inline)) {
+          constexpr int st = decltype(ss)::value;
+          constexpr int j = st / S::kOBlocks, bo = (st % S::kOBlocks) * 64;
+          vr[st % (VA + 1)][0] = lds_read_tr4_at<bo>(kt + v_rows[j][0]);
+          vr[st % (VA + 1)][1] = lds_read_tr4_at<bo>(kt + v_rows[j][1]);
+        };
+        static_for<VA>(read_v);
+        static_for<N>([&](auto ss) {
+          constexpr int st = decltype(ss)::value;
+          constexpr int issued = st + VA < N ? st + VA : N;
+          lds_wait<2 * (issued - 1 - st)>(vr[st % (VA + 1)][0], vr[st % (VA + 1)][1]);
+          o[st % S::kOBlocks] = mfma32(cat8(vr[st % (VA + 1)][0], vr[st % (VA + 1)][1]),
+                                       st / S::kOBlocks == 0 ? pf0 : pf1, o[st % S::kOBlocks]);
+          if constexpr (st + VA < N) read_v(std::integral_constant<int, st + VA>{});
+        });
       }
     }
   }
@@ -319,7 +401,7 @@ prefill_attention_kernel(const AttnParams p) {
   if (row_valid) {
     const int64_t orow = ((int64_t)split * p.num_tokens + token) * p.num_q_heads + head;
     if (p.out_f32) {
-      float* dst = static_cast<float*>(p.out) + orow * DV + half * 4;
+      float* dst = static_cast<float*>(p.out) + orow * D + half * 4;
 #pragma unroll
       for (int b = 0; b < S::kOBlocks; ++b)
 #pragma unroll
@@ -328,7 +410,7 @@ prefill_attention_kernel(const AttnParams p) {
               make_float4(o[b][4 * g] * inv, o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv,
                           o[b][4 * g + 3] * inv);
     } else {
-      uint16_t* dst = static_cast<uint16_t*>(p.out) + orow * DV + half * 4;
+      uint16_t* dst = static_cast<uint16_t*>(p.out) + orow * D + half * 4;
 #pragma unroll
       for (int b = 0; b < S::kOBlocks; ++b)
 #pragma unroll
@@ -348,14 +430,14 @@ bool prefill_supported(int head_dim_qk, int head_dim_v, int queries_per_kv, bool
          (head_dim_qk == 64 || head_dim_qk == 128 || head_dim_qk == 256);
 }
 
-template <int D, int DV>
+template <int D>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
-  using S = PrefillShape<D, DV>;
+  using S = PrefillShape<D>;
   const int block_q = S::kBlockM / p.queries_per_kv;
   const int gx = p.num_tokens / block_q + p.num_seqs;
   if (gx == 0) return hipSuccess;
-  const size_t lds = 2 * (S::kKBytes + S::kVBytes);
-  auto kern = prefill_attention_kernel<D, DV>;
+  const size_t lds = 2 * (size_t)S::kBufBytes;
+  auto kern = prefill_attention_kernel<D>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
@@ -366,9 +448,9 @@ static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
 
 hipError_t launch_attention_prefill(const AttnParams& p, hipStream_t stream) {
   switch (p.head_dim_qk) {
-    case 64: return launch_prefill_t<64, 64>(p, stream);
-    case 128: return launch_prefill_t<128, 128>(p, stream);
-    case 256: return launch_prefill_t<256, 256>(p, stream);
+    case 64: return launch_prefill_t<64>(p, stream);
+    case 128: return launch_prefill_t<128>(p, stream);
+    case 256: return launch_prefill_t<256>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
