@@ -15,10 +15,9 @@
 //   * KV tiles of 32 keys are gathered from the paged cache through the block
 //     table with direct-to-LDS 16-byte loads (global_load_lds_dwordx4), double
 //     buffered: the loads of tile t+1 are in flight while tile t is computed.
-//     The block-table entries of a tile are read with scalar loads one tile
-//     ahead, and a load's address is a scalar base (block, row group) plus a
-//     32-bit per-lane offset, so issuing a tile costs a few vector
-//     instructions.  Each load instruction writes whole rows as one block and
+//     The block-table entries of a tile are read one tile ahead, and a load's
+//     address is a scalar base (block, row group) plus a 32-bit per-lane
+//     offset, so issuing a tile costs a few vector instructions.  Each load instruction writes whole rows as one block and
 //     blocks are padded (K by 16 bytes, V by 64), so the K reads and the
 //     transposed V reads hit distinct banks while every LDS address is a lane
 //     base plus an immediate;
@@ -242,14 +241,17 @@ prefill_attention_kernel(const AttnParams p) {
     const bool lane_second = two_segs && rq >= 16;
     const uint32_t lane_off = (uint32_t)(((two_segs ? (rq & 15) : rq) * pitch) + dma_ch * 16);
 
-    // scalar block-table reads of a tile: the blocks of keys first and first + 16
-    auto tile_blocks = [&](int tile, int& b0, int& b1) __attribute__((always_inline)) {
-      const int first = tile * S::kTile;
-      b0 = load_uniform_i32(bt + (first >> bs_log2));
-      b1 = b0;
-      if (two_segs && first + 16 < seq_len) b1 = load_uniform_i32(bt + ((first + 16) >> bs_log2));
+    // Block-table entries of a tile's keys first (lane 0) and first + 16 (lane
+    // 1), read with a vector load one tile ahead: it is counted by vmcnt like
+    // the tile loads (the loop waits for both at its top), whereas a scalar
+    // load would share lgkmcnt with the LDS reads and stall their pipelines.
+    auto load_blocks = [&](int tile) __attribute__((always_inline)) -> int {
+      const int key = min(tile * S::kTile + (lane & 1) * 16, seq_len - 1);
+      return bt[key >> bs_log2];
     };
-    auto issue_tile = [&](int tile, int buf, int b0, int b1) __attribute__((always_inline)) {
+    auto issue_tile = [&](int tile, int buf, int blocks) __attribute__((always_inline)) {
+      const int b0 = __builtin_amdgcn_readlane(blocks, 0);
+      const int b1 = two_segs ? __builtin_amdgcn_readlane(blocks, 1) : b0;
       char* kt = smem + buf * S::kBufBytes;
       char* vt = kt + S::kKBytes;
       const int first = tile * S::kTile;
@@ -298,10 +300,8 @@ prefill_attention_kernel(const AttnParams p) {
     const uint32_t smem0 = lds_addr(smem);
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    int nb0, nb1;
-    tile_blocks(t_lo, nb0, nb1);
-    issue_tile(t_lo, 0, nb0, nb1);
-    if (t_lo + 1 < t_hi) tile_blocks(t_lo + 1, nb0, nb1);
+    issue_tile(t_lo, 0, load_blocks(t_lo));
+    int next_blocks = t_lo + 1 < t_hi ? load_blocks(t_lo + 1) : 0;
 
     for (int t = t_lo; t < t_hi; ++t) {
       const int buf = (t - t_lo) & 1;
@@ -311,8 +311,8 @@ prefill_attention_kernel(const AttnParams p) {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       lds_barrier();
       if (t + 1 < t_hi) {
-        issue_tile(t + 1, buf ^ 1, nb0, nb1);
-        if (t + 2 < t_hi) tile_blocks(t + 2, nb0, nb1);
+        issue_tile(t + 1, buf ^ 1, next_blocks);
+        if (t + 2 < t_hi) next_blocks = load_blocks(t + 2);
       }
       const int base = t * S::kTile;
       if (base > any_hi || base + S::kTile - 1 < any_lo) continue;  // no row of the wave sees it
