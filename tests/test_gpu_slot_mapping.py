@@ -102,3 +102,22 @@ def test_kv_cache_write_bit_exact(latent):
     if not latent:
         got_v = vc.view(torch.int16).cpu().numpy().view(np.uint16).reshape(v0.shape)
         assert np.array_equal(got_v, kv_cache_write_ref(v0, slots, v_new))
+
+
+@pytest.mark.parametrize("R", [1, 2, 63, 64, 65, 4095, 4096, 4097, 20000])
+def test_request_search_across_counts(R):
+    """Many short and empty requests: the request of each token is found by a
+    64-way search per wave (one to three rounds over these counts) and then a
+    per-lane walk across the request boundaries inside the lane's tokens."""
+    rng = np.random.default_rng(1000 + R)
+    B = 16
+    lens = rng.integers(0, 9, size=R) * (rng.random(R) > 0.3)
+    stride = 2
+    bt = rng.integers(0, 5000, size=(R, stride)).astype(np.int32)
+    qsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N = int(qsl[-1])
+    pos = rng.integers(0, stride * B, size=N).astype(np.int64)
+    M = N + 37
+    got = _gpu_slots(qsl, pos, bt, B, M)
+    ref = slot_mapping_ref(qsl, pos, bt, B, M)
+    assert np.array_equal(got, ref)
