@@ -19,21 +19,25 @@
 //   3. decode_merge_kernel merges the pieces of every item that spans several
 //      workgroups by their LSEs, and writes 0 / -inf for items without tiles.
 //
-// Inside a workgroup (NHB * 32 query heads, two waves per 32-head block):
+// Inside a workgroup, 128 query heads per KV head (decode_full_kernel): four
+// waves, one per SIMD, wave w owns heads [32 w, 32 w + 32) over the whole row:
 //   * tiles of 32 keys are gathered once per workgroup into LDS with
-//     direct-to-LDS 16-byte loads, double buffered (tile t+1 and the block-table
-//     reads of tile t+2 are in flight while tile t is computed).  LDS-DMA
-//     instruction c moves the 16-wide k-chunk c of all 32 keys as one block, so
-//     a K read for k-chunk c and the transposed V reads are a lane base plus an
-//     immediate;
-//   * S^T[32 keys][32 heads] = K Q^T is split over the 576-long dot product:
-//     wave (hb, 0) sums k-chunks 0..17 and wave (hb, 1) k-chunks 18..35, each
-//     with its Q fragments in registers; the halves are exchanged through LDS
-//     and both waves add them in the same order, so they hold identical scores;
-//   * both waves run the same online softmax; wave (hb, d) then accumulates
-//     O^T += V^T P^T for output columns [256 d, 256 d + 256), reading V^T out of
-//     the same K tile with ds_read_b64_tr_b16;
+//     direct-to-LDS 16-byte loads in a three-deep ring; LDS-DMA instruction c
+//     moves the 16-wide k-chunk c of all 32 keys as one block, so a K read for
+//     k-chunk c and the transposed V reads are a lane base plus an immediate.
+//     The DMA of tile t + 2 is spread over the score MFMAs of tile t (issued all
+//     at once after the barrier, the four waves stall on the shared address
+//     unit), and the block-table entry of a tile is read a tile ahead;
+//   * S^T[32 keys][32 heads] = K Q^T over all 36 k-chunks, Q in registers;
+//   * online softmax, then O^T += V^T P^T over all 512 output columns, V^T read
+//     out of the same K tile with ds_read_b64_tr_b16.  The 16 output blocks
+//     (256 fp32 per lane) live in the AGPRs, managed by inline assembly;
 //   * the running max moves only when it grows by more than 2^8 (log2 units).
+// With 32 or 64 heads per KV head (decode_attention_kernel) two waves share a
+// 32-head block: wave (hb, 0) sums k-chunks 0..17 and wave (hb, 1) k-chunks
+// 18..35, the halves are exchanged through LDS and added in the same order by
+// both, both run the same softmax, and wave (hb, d) accumulates output columns
+// [256 d, 256 d + 256).
 // The mask (window, image ranges, key range of the split) is applied exactly
 // as in the prefill kernel; one query position per item makes it uniform.
 #include "device_common.h"
@@ -51,10 +55,6 @@ constexpr int kTileBytes = kKChunks * kBlock;
 constexpr int kOBlocks = kDV / 2 / 32;      // 8 blocks of 32 output columns per wave
 constexpr int kPlanThreads = 1024;
 }  // namespace dec
-
-#ifndef DEC_NB
-#define DEC_NB 1
-#endif
 
 // One (token, split) work item: its request and the tiles / keys its row may see.
 struct DecodeItem {
@@ -156,6 +156,141 @@ __device__ __forceinline__ void dec_dma16(const void* gsrc, void* lds_dst) {
       (const __attribute__((address_space(1))) void*)gsrc,
       (__attribute__((address_space(3))) void*)(lds_void*)lds_dst, 16, 0, 0);
 }
+
+namespace dec {
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+// LDS reads the compiler does not track: the result may be consumed only after
+// lds_wait<N>() on it, which waits until at most N LDS operations of this wave
+// are outstanding (they complete in issue order) and ties the registers to it.
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_read_b128_at(uint32_t addr) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ bf16x4 lds_read_tr4_at(uint32_t addr) {
+  i16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return __builtin_bit_cast(bf16x4, r);
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(bf16x8& a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N < 15 ? N : 15));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(bf16x4& a, bf16x4& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N < 15 ? N : 15));
+}
+// max / sum of the values of lanes l and l ^ 32, in every lane (one
+// v_permlane32_swap instead of an LDS permute); both lanes of a pair get the
+// same, order-independent result.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// A vector load the compiler does not track (so it adds no vmcnt(0) waits of
+// its own around the LDS-DMA pipeline): the result may be used only after
+// vm_wait_tied<N>(), which waits until at most N vector-memory operations of
+// this wave are outstanding (loads complete in issue order) and ties the
+// register to that point.  The memory clobber keeps the load in program order
+// with the LDS-DMA instructions.
+__device__ __forceinline__ int load_i32_async(const int32_t* ptr) {
+  int r;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(ptr) : "memory");
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void vm_wait_tied(int& r) {
+  asm volatile("s_waitcnt vmcnt(%1)" : "+v"(r) : "i"(N));
+}
+
+// Output accumulators of the full-width kernel: AGPRs a0..a255, block b (32
+// output columns x 32 heads, the MFMA's 16 result registers) in
+// a[16 b .. 16 b + 15].  Only the inline assembly below writes or reads them:
+// the kernel's other values stay below 256 VGPRs, so the compiler allocates
+// no AGPR of its own (a build check verifies this), and the clobber of a255
+// makes it reserve all 256.  The compiler does not see the MFMAs inside the
+// assembly, so the wait states it would insert are written out: two before an
+// MFMA whose sources a VALU instruction may just have written, and 16 or more
+// between an MFMA and a VALU read of its result.
+__device__ __forceinline__ void oacc_zero() {
+  asm volatile(
+      ".set psw_r, 0\n.rept 256\n"
+      "v_accvgpr_write_b32 a[psw_r], 0\n"
+      ".set psw_r, psw_r + 1\n.endr" ::: "a255");
+}
+template <int B>
+__device__ __forceinline__ void oacc_mfma(const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[%2:%3], %0, %1, a[%2:%3]"
+               :: "v"(a), "v"(b), "i"(16 * B), "i"(16 * B + 15));
+}
+__device__ __forceinline__ void oacc_settle() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+}
+// every accumulator times alpha, two registers at a time
+__device__ __forceinline__ void oacc_scale(float alpha) {
+  float t0, t1;
+  asm volatile(
+      "s_nop 7\n\ts_nop 7\n\ts_nop 3\n"
+      ".set psw_r, 0\n.rept 128\n"
+      "v_accvgpr_read_b32 %0, a[psw_r]\n"
+      "v_accvgpr_read_b32 %1, a[psw_r + 1]\n"
+      "v_mul_f32 %0, %0, %2\n"
+      "v_mul_f32 %1, %1, %2\n"
+      "v_accvgpr_write_b32 a[psw_r], %0\n"
+      "v_accvgpr_write_b32 a[psw_r + 1], %1\n"
+      ".set psw_r, psw_r + 2\n.endr"
+      : "=&v"(t0), "=&v"(t1)
+      : "v"(alpha));
+}
+// accumulator block B as 16 floats; the memory clobber keeps the stores of
+// earlier blocks before these reads
+template <int B>
+__device__ __forceinline__ f32x16 oacc_get() {
+  f32x16 v;
+  static_for<16>([&](auto ii) {
+    constexpr int i = decltype(ii)::value;
+    float x;
+    asm volatile("v_accvgpr_read_b32 %0, a[%1]" : "=v"(x) : "i"(16 * B + i) : "memory");
+    v[i] = x;
+  });
+  return v;
+}
+
+// The score MFMAs as inline assembly with the accumulator in VGPRs (the
+// builtin would put it in AGPRs beside the 256 output accumulators).  The
+// compiler does not see these as MFMAs, so the wait states it would insert
+// are written here: two before each MFMA (a VALU write of a source operand),
+// and after the chain enough for the VALU to read the result.  The s_nop
+// before a dependent MFMA overlaps the previous MFMA's execution.
+__device__ __forceinline__ f32x16 mfma32_vgpr_first(const bf16x8& a, const bf16x8& b) {
+  f32x16 d;
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+               : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma32_vgpr(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+               : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vgpr_settle(f32x16& d) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d));
+}
+}  // namespace dec
 
 // Where the stream-K pieces live inside the caller's workspace.
 struct DecodeWork {
@@ -483,6 +618,287 @@ void decode_attention_kernel(const AttnParams p, const DecodeWork wk) {
   }
 }
 
+// Full-width variant for 128 query heads: 4 waves, one per SIMD, wave w owns
+// heads [32 w, 32 w + 32) over the whole row: S^T over all 36 k-chunks (Q held
+// in registers, 144 VGPRs) and O^T over all 512 output columns (256 AGPRs), so
+// no half-scores are exchanged and no softmax is computed twice.  Each wave
+// has 68 MFMAs per tile, against one softmax, one barrier and nine LDS-DMA
+// instructions; the K and V^T reads run a few steps ahead of their MFMAs.
+template <bool UNIFORM_BT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_full_kernel(const AttnParams p, const DecodeWork wk) {
+  using namespace dec;
+  constexpr int kWaves = 4;
+  constexpr int kHeads = 128;
+  constexpr int kDmaPerWave = kKChunks / kWaves;  // 9
+  static_assert(kDmaPerWave * kWaves == kKChunks, "k-chunks split evenly over the waves");
+  constexpr int kOB = kDV / 32;                    // 16 output blocks of 32 columns
+  constexpr int kBufs = UNIFORM_BT ? 3 : 2;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: keep it scalar
+  const int half = lane >> 5;
+  const int G = wk.grid;
+  const int groups = gridDim.y;
+  const int logical = xcd_logical_id(blockIdx.x + gridDim.x * blockIdx.y, G * groups);
+  const int w = logical % G;       // neighbouring w share items: keep them on one XCD
+  const int group = logical / G;
+  const int head0 = group * kHeads;
+  const int kvh = head0 / p.queries_per_kv;
+
+  const int items = p.num_tokens * p.num_splits;
+  const int total = wk.prefix[items];
+  const int per = max(1, (total + G - 1) / G);
+  const int g0 = w * per, g1 = min(total, g0 + per);
+  if (g0 >= g1) return;
+  int it;
+  {
+    int lo = 0, hi = items - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (wk.prefix[mid] <= g0) lo = mid; else hi = mid - 1;
+    }
+    it = lo;
+  }
+
+  const int hl = wave * 32 + (lane & 31);  // head of this lane inside the group
+  const int64_t slot_pitch = (int64_t)p.num_kv_heads * kD;
+  const uint16_t* kbase = p.k_cache + (int64_t)kvh * kD;
+  const int bs_log2 = p.block_size_log2;
+  const int bs_mask = (1 << bs_log2) - 1;
+  const float c2 = p.scale_log2;
+  const int dma_hh = lane >> 5;
+  const int dma_row = (lane - 4 * dma_hh) & 31;
+  const int tr_key = half * 4 + ((lane & 15) >> 2);
+  const int tr_g = (lane >> 4) & 1;
+  const int tr_hh = (lane & 3) >> 1, tr_in = (lane & 1) * 8;
+  const int dcol = half * 4;
+  const uint32_t smem0 = lds_addr(smem);
+  const uint32_t k_lane = (uint32_t)(dec_slot(lane & 31, half) * 16);
+  uint32_t v_lane[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    v_lane[j][0] = (uint32_t)(tr_g * kBlock + tr_in + dec_slot(16 * j + tr_key, tr_hh) * 16);
+    v_lane[j][1] = (uint32_t)(tr_g * kBlock + tr_in + dec_slot(16 * j + tr_key + 8, tr_hh) * 16);
+  }
+
+  int g = g0;
+  while (true) {
+    const int p0 = wk.prefix[it], p1 = wk.prefix[it + 1];
+    const DecodeItem d = decode_item(p, it);
+    // previous item: all waves done with LDS, all stores and loads retired
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // Q is loaded per item (not kept across items: the registers are needed
+    // by the epilogue)
+    bf16x8 qf[kKChunks];
+    {
+      const uint16_t* qrow = p.q + ((int64_t)d.token * p.num_q_heads + head0 + hl) * kD + half * 8;
+#pragma unroll
+      for (int c = 0; c < kKChunks; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qrow + c * 16);
+    }
+    const int t_first = d.t_lo + (g - p0);
+    const int t_end = d.t_lo + (min(g1, p1) - p0);
+    const int seq_len = d.seq_len;
+    const int row_lo = d.row_lo, row_hi = d.row_hi;
+    const int32_t* bt = p.block_table + (int64_t)d.seq * p.block_table_stride;
+
+    oacc_zero();
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // The LDS-DMA of one tile: this wave moves k-chunks wave, wave + 4, ...
+    // Rows past the last key repeat the last key (finite values, masked later).
+    // dma_src() gives this lane's source row for the tile; chunk c then adds
+    // c * 16 elements.
+    auto dma_src = [&](int tile, int blk) __attribute__((always_inline)) {
+      const int first = tile * kTile;
+      if constexpr (UNIFORM_BT) {
+        // uniform block entry blk + a per-lane 32-bit offset (row, column half)
+        const char* tile_base = reinterpret_cast<const char*>(
+            kbase + (((int64_t)blk << bs_log2) + (first & bs_mask)) * slot_pitch);
+        const uint32_t row = (uint32_t)min(dma_row, seq_len - 1 - first);
+        return reinterpret_cast<const uint16_t*>(
+            tile_base + (row * (uint32_t)slot_pitch + (uint32_t)dma_hh * 8u) * 2u);
+      } else {
+        const int key = min(first + dma_row, seq_len - 1);
+        const int b = bt[key >> bs_log2];
+        return kbase + (((int64_t)b << bs_log2) + (key & bs_mask)) * slot_pitch + dma_hh * 8;
+      }
+    };
+    auto dma_chunk = [&](const uint16_t* src, int buf, int i) __attribute__((always_inline)) {
+      const int c = i * kWaves + wave;
+      dec_dma16(src + c * 16, smem + buf * kTileBytes + c * kBlock);
+    };
+    auto issue_tile = [&](int tile, int buf, int blk) __attribute__((always_inline)) {
+      const uint16_t* src = dma_src(tile, blk);
+#pragma unroll
+      for (int i = 0; i < kDmaPerWave; ++i) dma_chunk(src, buf, i);
+    };
+
+    // UNIFORM_BT: a 3-deep ring.  In iteration t the DMA of tile t + 2 is
+    // spread over the score MFMAs (all four waves issuing their nine
+    // instructions at once stall on the shared address unit).  Past the last
+    // tile the ring reloads the last tile into the free buffer, so that every
+    // iteration has the same outstanding operations.  The block-table entry of
+    // tile u + 1 is read with an untracked vector load just before the DMA of
+    // tile u and consumed an iteration later; a scalar load there would be
+    // waited for on the spot.
+    auto bt_entry = [&](int tile) __attribute__((always_inline)) {
+      return load_i32_async(bt + ((min(tile, t_end - 1) * kTile) >> bs_log2));
+    };
+    int bt_next = 0;
+    if constexpr (UNIFORM_BT) {
+      issue_tile(t_first, 0, load_uniform_i32(bt + ((t_first * kTile) >> bs_log2)));
+      const int t1 = min(t_first + 1, t_end - 1);
+      const int blk1 = load_uniform_i32(bt + ((t1 * kTile) >> bs_log2));
+      bt_next = bt_entry(t_first + 2);
+      issue_tile(t1, 1, blk1);
+    } else {
+      issue_tile(t_first, 0, 0);
+    }
+
+    for (int t = t_first; t < t_end; ++t) {
+      const int buf = (t - t_first) % kBufs;
+      const int nbuf = (buf + kBufs - 1) % kBufs;  // last read in iteration t - 1
+      const uint16_t* nsrc = nullptr;
+      if constexpr (UNIFORM_BT) {
+        // tile t landed; the entry load and the nine DMAs issued after it
+        // (tile t + 1, or a repeat of the last tile) may still be in flight
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerWave + 1));
+        lds_barrier();
+        vm_wait_tied<kDmaPerWave>(bt_next);  // older than the 9 DMAs of tile t + 1
+        const int blk = __builtin_amdgcn_readfirstlane(bt_next);
+        bt_next = bt_entry(t + 3);
+        nsrc = dma_src(min(t + 2, t_end - 1), blk);
+      } else {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        lds_barrier();
+        if (t + 1 < t_end) issue_tile(t + 1, nbuf, 0);
+      }
+      const uint32_t kt = smem0 + (uint32_t)(buf * kTileBytes);
+
+      // S^T[32 keys][32 heads] over the 36 k-chunks, K reads KA ahead; with
+      // UNIFORM_BT one DMA instruction of tile t + 2 after every fourth MFMA
+      f32x16 s;
+      {
+        constexpr int N = kKChunks, KA = 3;
+        const uint32_t ka = kt + k_lane;
+        bf16x8 kf[KA + 1];
+        static_for<KA>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          kf[c] = lds_read_b128_at<c * kBlock>(ka);
+        });
+        static_for<N>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          constexpr int issued = c + KA < N ? c + KA : N;
+          lds_wait<issued - 1 - c>(kf[c % (KA + 1)]);
+          if constexpr (c == 0) s = mfma32_vgpr_first(kf[0], qf[0]);
+          else mfma32_vgpr(s, kf[c % (KA + 1)], qf[c]);
+          if constexpr (c + KA < N)
+            kf[(c + KA) % (KA + 1)] = lds_read_b128_at<(c + KA) * kBlock>(ka);
+          if constexpr (UNIFORM_BT && c % 4 == 0) dma_chunk(nsrc, nbuf, c / 4);
+        });
+        mfma_vgpr_settle(s);
+      }
+
+      const int base = t * kTile;
+      if (!(base >= row_lo && base + kTile - 1 <= row_hi)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int k = base + (i / 4) * 8 + half * 4 + (i % 4);
+          s[i] = (k >= row_lo && k <= row_hi) ? s[i] : -INFINITY;
+        }
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+      mx = pair_max(mx) * c2;
+      if (__ballot(mx > m_run + 8.f) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+        oacc_scale(alpha);
+        m_run = m_new;
+      }
+      const float m_sub = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = fast_exp2(fmaf(s[i], c2, -m_sub));
+      const bf16x8 pf0 = to_bf16x8(s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]);
+      const bf16x8 pf1 = to_bf16x8(s[8], s[9], s[10], s[11], s[12], s[13], s[14], s[15]);
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      static_for<4>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf0, pf0, 2 * i, 2 * i + 1),
+                                                ones, l_run, false);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf1, pf1, 2 * i, 2 * i + 1),
+                                                ones, l_run, false);
+      });
+
+      // O^T += V^T P^T: step st covers output block b = st % 16 (columns 32 b +
+      // [0, 32), k-chunks 2 b + tr_g) and keys 16 j + [0, 16), j = st / 16;
+      // the transposed reads run VA steps ahead
+      {
+        constexpr int N = 2 * kOB, VA = 2;
+        bf16x4 vr[VA + 1][2];
+        auto read_v = [&](auto ss) __attribute__((always_inline)) {
+          constexpr int st = decltype(ss)::value;
+          constexpr int j = st / kOB, bo = (st % kOB) * 2 * kBlock;
+          vr[st % (VA + 1)][0] = lds_read_tr4_at<bo>(kt + v_lane[j][0]);
+          vr[st % (VA + 1)][1] = lds_read_tr4_at<bo>(kt + v_lane[j][1]);
+        };
+        static_for<VA>(read_v);
+        static_for<N>([&](auto ss) {
+          constexpr int st = decltype(ss)::value;
+          constexpr int issued = st + VA < N ? st + VA : N;
+          lds_wait<2 * (issued - 1 - st)>(vr[st % (VA + 1)][0], vr[st % (VA + 1)][1]);
+          oacc_mfma<st % kOB>(cat8(vr[st % (VA + 1)][0], vr[st % (VA + 1)][1]),
+                              st / kOB == 0 ? pf0 : pf1);
+          if constexpr (st + VA < N) read_v(std::integral_constant<int, st + VA>{});
+        });
+      }
+    }
+
+    const bool complete = p0 >= g0 && p1 <= g1;
+    const float l_tot = pair_sum(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse_val = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    // final rows of an item inside this workgroup's range, else a piece of an
+    // item shared with neighbouring workgroups (fp32, merged later)
+    const int64_t orow = ((int64_t)d.split * p.num_tokens + d.token) * p.num_q_heads + head0 + hl;
+    const int64_t prow = ((int64_t)group * 2 * G + (p0 < g0 ? 2 * w : 2 * w + 1)) * kHeads + hl;
+    const bool as_bf16 = complete && !p.out_f32;
+    float* dst32 = complete ? static_cast<float*>(p.out) + orow * kDV + dcol
+                            : wk.piece_o + prow * kDV + dcol;
+    uint16_t* dst16 = static_cast<uint16_t*>(p.out) + orow * kDV + dcol;
+    oacc_settle();
+    static_for<kOB>([&](auto bb) {
+      constexpr int b = decltype(bb)::value;
+      const f32x16 v = oacc_get<b>();
+      if (as_bf16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<bf16x4*>(dst16 + b * 32 + q * 8) =
+              to_bf16x4(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(dst32 + b * 32 + q * 8) =
+              make_float4(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
+      }
+    });
+    if (half == 0) {
+      if (!complete) wk.piece_lse[prow] = lse_val;
+      else if (p.lse != nullptr) p.lse[orow] = lse_val;
+    }
+
+    g = min(g1, p1);
+    if (g >= g1) break;
+    ++it;
+    while (wk.prefix[it + 1] <= g) ++it;  // skip items without tiles
+  }
+}
+
 // One wave per (item, head): merge the pieces of items that span several
 // workgroups (LSE-weighted, as the combine step does), and write 0 / -inf for
 // items without tiles.  Items inside one workgroup's range are already final.
@@ -602,9 +1018,21 @@ hipError_t launch_decode_t(const AttnParams& p, const DecodeWork& wk, hipStream_
 }
 
 template <bool UNIFORM_BT>
+hipError_t launch_decode_full(const AttnParams& p, const DecodeWork& wk, hipStream_t stream) {
+  constexpr int kBufs = UNIFORM_BT ? 3 : 2;
+  const size_t lds = kBufs * dec::kTileBytes;
+  auto kern = decode_full_kernel<UNIFORM_BT>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(wk.grid, p.num_q_heads / 128), dim3(256), lds, stream, p, wk);
+  return hipGetLastError();
+}
+
+template <bool UNIFORM_BT>
 hipError_t launch_decode_shape(const AttnParams& p, int heads, const DecodeWork& wk,
                                hipStream_t stream) {
-  if (heads == 128) return launch_decode_t<DEC_NB, 4 / DEC_NB, UNIFORM_BT>(p, wk, stream);
+  if (heads == 128) return launch_decode_full<UNIFORM_BT>(p, wk, stream);
   if (heads == 64) return launch_decode_t<2, 1, UNIFORM_BT>(p, wk, stream);
   return launch_decode_t<1, 1, UNIFORM_BT>(p, wk, stream);
 }

@@ -1,0 +1,61 @@
+"""Invariants of the generated gfx950 code that the kernels rely on.
+
+The full-width latent decode kernel keeps its 256 output accumulators in AGPRs
+that only its inline assembly touches; this holds only while the compiler
+allocates no AGPR of its own in that kernel (its other values must stay below
+256 VGPRs).  The check compiles the source to assembly and looks for AGPR
+operands outside the inline-assembly regions.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(ROOT, "paged_sliding_window_amd", "csrc", "attention_decode.hip")
+
+
+def _hipcc():
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    return None
+
+
+def _kernel_bodies(asm: str, prefix: str):
+    for m in re.finditer(r"^(%s\w*):" % re.escape(prefix), asm, re.M):
+        end = asm.index("s_endpgm", m.end())
+        yield m.group(1), asm[m.end():end]
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+def test_full_width_decode_leaves_agprs_to_inline_asm(tmp_path):
+    import paged_sliding_window_amd.build as b
+    out = tmp_path / "dec.s"
+    cmd = [_hipcc(), *b.HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-S",
+           "--cuda-device-only", SRC, "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    asm = out.read_text()
+    bodies = list(_kernel_bodies(asm, "_ZN3psw18decode_full_kernel"))
+    assert len(bodies) == 2, [n for n, _ in bodies]  # block-table variants
+    for name, body in bodies:
+        in_asm = False
+        for line in body.split("\n"):
+            t = line.strip()
+            if t.startswith(";;#ASMSTART"):
+                in_asm = True
+                continue
+            if t.startswith(";;#ASMEND"):
+                in_asm = False
+                continue
+            if in_asm or t.startswith(";") or t.startswith("."):
+                continue
+            code = t.split(";")[0]
+            assert not re.search(r"\ba\d+\b|\ba\[\d+", code), f"{name}: compiler AGPR use: {t}"
+        assert "scratch_" not in body, f"{name}: register spills"
+    # the kernel descriptors reserve all 256 AGPRs (the clobber of a255)
+    assert len(re.findall(r"\.agpr_count:\s+256", asm)) >= 2
