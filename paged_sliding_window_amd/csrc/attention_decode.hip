@@ -40,6 +40,8 @@
 // [256 d, 256 d + 256).
 // The mask (window, image ranges, key range of the split) is applied exactly
 // as in the prefill kernel; one query position per item makes it uniform.
+#include <type_traits>
+
 #include "device_common.h"
 #include "psw_internal.h"
 
@@ -61,6 +63,9 @@ struct DecodeItem {
   int token, split, seq, seq_len, t_lo, t_hi, row_lo, row_hi;
 };
 
+// WAVE: called by a whole wave for one item (all lanes active), so the image
+// ranges are walked in the wave form; otherwise one item per thread.
+template <bool WAVE>
 __device__ __forceinline__ DecodeItem decode_item(const AttnParams& p, int item) {
   DecodeItem d;
   d.token = item / p.num_splits;
@@ -84,15 +89,15 @@ __device__ __forceinline__ DecodeItem decode_item(const AttnParams& p, int item)
     key_begin = max(0, p.key_ranges[kr]);
     key_end = min(d.seq_len, p.key_ranges[kr + 1]);
   }
+  using R = std::conditional_t<WAVE, RangesWave, RangesPtr>;
+  const R rg{ranges, p.max_mm_ranges};
   int64_t lo64, hi64;
-  row_interval((int64_t)ctx + qpos, d.seq_len, p.geom, ranges, p.max_mm_ranges, key_begin,
-               key_end, lo64, hi64);
+  row_interval_r((int64_t)ctx + qpos, d.seq_len, p.geom, rg, key_begin, key_end, lo64, hi64);
   if (lo64 <= hi64) {
     // the row's allowed keys are one interval; its tiles are inside the query
     // block's tile bounds, which are kept as the outer limit
-    const TileRange tr = tile_bounds(ctx, d.seq_len, query_len, qpos, dec::kTile,
-                                     p.queries_per_kv, 1, p.queries_per_kv, p.geom, ranges,
-                                     p.max_mm_ranges);
+    const TileRange tr = tile_bounds_r(ctx, d.seq_len, query_len, qpos, dec::kTile,
+                                       p.queries_per_kv, 1, p.queries_per_kv, p.geom, rg);
     d.row_lo = (int)lo64;
     d.row_hi = (int)hi64;
     d.t_lo = max(tr.lo, d.row_lo / dec::kTile);
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(dec::kPlanThreads) void decode_plan_kernel(const At
     const int it = base + tid;
     int cnt = 0;
     if (it < items) {
-      const DecodeItem d = decode_item(p, it);
+      const DecodeItem d = decode_item<false>(p, it);
       cnt = d.t_hi - d.t_lo;
     }
     int x = cnt;  // inclusive scan inside the wave
@@ -368,7 +373,7 @@ void decode_attention_kernel(const AttnParams p, const DecodeWork wk) {
   int g = g0;
   while (true) {
     const int p0 = wk.prefix[it], p1 = wk.prefix[it + 1];
-    const DecodeItem d = decode_item(p, it);
+    const DecodeItem d = decode_item<true>(p, it);
     // previous item: all waves done with LDS, all stores and loads retired
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -686,7 +691,7 @@ void decode_full_kernel(const AttnParams p, const DecodeWork wk) {
   int g = g0;
   while (true) {
     const int p0 = wk.prefix[it], p1 = wk.prefix[it + 1];
-    const DecodeItem d = decode_item(p, it);
+    const DecodeItem d = decode_item<true>(p, it);
     // previous item: all waves done with LDS, all stores and loads retired
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

@@ -165,8 +165,9 @@ prefill_attention_kernel(const AttnParams p) {
     key_begin = max(0, p.key_ranges[((int64_t)split * p.num_seqs + seq) * 2]);
     key_end = min(seq_len, p.key_ranges[((int64_t)split * p.num_seqs + seq) * 2 + 1]);
   }
-  const TileRange tr = tile_bounds(ctx, seq_len, query_len, q_block, S::kTile, block_q * qpk,
-                                   block_q, qpk, p.geom, ranges, p.max_mm_ranges);
+  const RangesWave rg{ranges, p.max_mm_ranges};  // every lane is active here
+  const TileRange tr = tile_bounds_r(ctx, seq_len, query_len, q_block, S::kTile, block_q * qpk,
+                                     block_q, qpk, p.geom, rg);
   const int t_lo = max(tr.lo, key_begin / S::kTile);
   const int t_hi = min(tr.hi, (key_end + S::kTile - 1) / S::kTile);
 
@@ -178,11 +179,11 @@ prefill_attention_kernel(const AttnParams p) {
   const bool row_valid = pos_in_blk < block_q && qpos < query_len;
   const int64_t token = (int64_t)q_start + qpos;
   int row_lo = INT32_MAX, row_hi = INT32_MIN;
-  if (row_valid) {
+  {
+    // computed by every lane (the wave form of the range walk needs them all)
     int64_t lo64, hi64;
-    row_interval((int64_t)ctx + qpos, seq_len, p.geom, ranges, p.max_mm_ranges, key_begin,
-                 key_end, lo64, hi64);
-    if (lo64 <= hi64) {
+    row_interval_r((int64_t)ctx + qpos, seq_len, p.geom, rg, key_begin, key_end, lo64, hi64);
+    if (row_valid && lo64 <= hi64) {
       row_lo = (int)lo64;
       row_hi = (int)hi64;
     }
@@ -249,27 +250,47 @@ prefill_attention_kernel(const AttnParams p) {
       const int key = min(tile * S::kTile + (lane & 1) * 16, seq_len - 1);
       return bt[key >> bs_log2];
     };
-    auto issue_tile = [&](int tile, int buf, int blocks) __attribute__((always_inline)) {
+    // Fast path of a tile's DMA: every instruction is a scalar base (lo) plus
+    // one 32-bit offset per lane (voff).
+    struct DmaPlan {
+      int64_t lo;
+      uint32_t voff;
+      bool fast;
+    };
+    auto plan_tile = [&](int tile, int blocks) __attribute__((always_inline)) {
       const int b0 = __builtin_amdgcn_readlane(blocks, 0);
       const int b1 = two_segs ? __builtin_amdgcn_readlane(blocks, 1) : b0;
-      char* kt = smem + buf * S::kBufBytes;
-      char* vt = kt + S::kKBytes;
       const int first = tile * S::kTile;
       // byte offsets of the two segments in the cache (first row of each)
       const int64_t seg0 = (((int64_t)b0 << bs_log2) + (first & bs_mask)) * pitch;
       const int64_t seg1 = ((int64_t)b1 << bs_log2) * pitch;
-      const int64_t lo = two_segs ? min(seg0, seg1) : seg0;
-      const int64_t delta = two_segs ? max(seg0, seg1) - lo : 0;
-      if (fast_blocks && first + S::kTile <= seq_len && delta < ((int64_t)1 << 31)) {
-        // scalar base + one 32-bit offset per lane for every instruction
-        const bool lane_far = lane_second ? seg1 > seg0 : seg0 > seg1;
-        const uint32_t voff = lane_off + (lane_far ? (uint32_t)delta : 0u);
+      DmaPlan d;
+      d.lo = two_segs ? min(seg0, seg1) : seg0;
+      const int64_t delta = two_segs ? max(seg0, seg1) - d.lo : 0;
+      d.fast = fast_blocks && first + S::kTile <= seq_len && delta < ((int64_t)1 << 31);
+      const bool lane_far = lane_second ? seg1 > seg0 : seg0 > seg1;
+      d.voff = lane_off + (lane_far ? (uint32_t)delta : 0u);
+      return d;
+    };
+    // instruction i of this wave (K, then V), fast path
+    auto dma_k = [&](const DmaPlan& d, int buf, int i) __attribute__((always_inline)) {
+      const int g = wave * S::kInstrPerWave + i;
+      lds_dma16(kbase + d.lo + g * pitch + d.voff, smem + buf * S::kBufBytes + g * S::kKBlock);
+    };
+    auto dma_v = [&](const DmaPlan& d, int buf, int i) __attribute__((always_inline)) {
+      const int g = wave * S::kInstrPerWave + i;
+      lds_dma16(vbase + d.lo + g * pitch + d.voff,
+                smem + buf * S::kBufBytes + S::kKBytes + g * S::kVBlock);
+    };
+    auto issue_tile = [&](int tile, int buf, const DmaPlan& d) __attribute__((always_inline)) {
+      char* kt = smem + buf * S::kBufBytes;
+      char* vt = kt + S::kKBytes;
+      const int first = tile * S::kTile;
+      if (d.fast) {
 #pragma unroll
         for (int i = 0; i < S::kInstrPerWave; ++i) {
-          const int g = wave * S::kInstrPerWave + i;
-          const int64_t row = lo + g * pitch;
-          lds_dma16(kbase + row + voff, kt + g * S::kKBlock);
-          lds_dma16(vbase + row + voff, vt + g * S::kVBlock);
+          dma_k(d, buf, i);
+          dma_v(d, buf, i);
         }
       } else {
         // last tile (rows past the end repeat the last key: finite data,
@@ -300,8 +321,14 @@ prefill_attention_kernel(const AttnParams p) {
     const uint32_t smem0 = lds_addr(smem);
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    issue_tile(t_lo, 0, load_blocks(t_lo));
-    int next_blocks = t_lo + 1 < t_hi ? load_blocks(t_lo + 1) : 0;
+    // Pipeline: the block-table entries of tile u are read in iteration u - 3,
+    // its DMA plan is computed between the output MFMAs of iteration u - 2 (in
+    // their shadow), and its DMA is issued in iteration u - 1.
+    issue_tile(t_lo, 0, plan_tile(t_lo, load_blocks(t_lo)));
+    DmaPlan nd;  // plan of tile t + 1
+    nd.fast = false;
+    if (t_lo + 1 < t_hi) nd = plan_tile(t_lo + 1, load_blocks(t_lo + 1));
+    int blk_next = t_lo + 2 < t_hi ? load_blocks(t_lo + 2) : 0;  // entries of tile t + 2
 
     for (int t = t_lo; t < t_hi; ++t) {
       const int buf = (t - t_lo) & 1;
@@ -310,12 +337,19 @@ prefill_attention_kernel(const AttnParams p) {
       // before it is refilled
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       lds_barrier();
-      if (t + 1 < t_hi) {
-        issue_tile(t + 1, buf ^ 1, next_blocks);
-        if (t + 2 < t_hi) next_blocks = load_blocks(t + 2);
-      }
       const int base = t * S::kTile;
-      if (base > any_hi || base + S::kTile - 1 < any_lo) continue;  // no row of the wave sees it
+      const bool skip = base > any_hi || base + S::kTile - 1 < any_lo;  // no row of the wave sees it
+      // The fast-path DMA of tile t + 1 is spread over the score MFMAs below
+      // (all waves issuing right after the barrier stall on the shared address
+      // unit); the other cases issue it here.
+      const int blk_after = t + 3 < t_hi ? load_blocks(t + 3) : 0;  // entries of tile t + 3
+      if (t + 1 < t_hi && (!nd.fast || skip)) issue_tile(t + 1, buf ^ 1, nd);
+      const bool inter = t + 1 < t_hi && nd.fast;
+      if (skip) {
+        if (t + 2 < t_hi) nd = plan_tile(t + 2, blk_next);
+        blk_next = blk_after;
+        continue;
+      }
       const uint32_t kt = smem0 + (uint32_t)(buf * S::kBufBytes);
 
       // S^T[key][row] for the 32 keys; K k-chunks read KA ahead
@@ -335,6 +369,12 @@ prefill_attention_kernel(const AttnParams p) {
           lds_wait<issued - 1 - c>(kf[c % (KA + 1)]);
           s = mfma32(kf[c % (KA + 1)], qf[c], s);
           if constexpr (c + KA < N) kf[(c + KA) % (KA + 1)] = lds_read_b128_at<(c + KA) * 32>(ka);
+          constexpr int step = N / S::kInstrPerWave;
+          if constexpr (c % step == 0) {
+            if (inter) dma_k(nd, buf ^ 1, c / step);
+          } else if constexpr (c % step == step / 2) {
+            if (inter) dma_v(nd, buf ^ 1, c / step);
+          }
         });
       }
       if (!(base >= wave_lo && base + S::kTile - 1 <= wave_hi)) {
@@ -390,8 +430,11 @@ prefill_attention_kernel(const AttnParams p) {
           o[st % S::kOBlocks] = mfma32(cat8(vr[st % (VA + 1)][0], vr[st % (VA + 1)][1]),
                                        st / S::kOBlocks == 0 ? pf0 : pf1, o[st % S::kOBlocks]);
           if constexpr (st + VA < N) read_v(std::integral_constant<int, st + VA>{});
+          // (unused when t + 2 >= t_hi: no branch inside the MFMA sequence)
+          if constexpr (st == 1) nd = plan_tile(t + 2, blk_next);
         });
       }
+      blk_next = blk_after;
     }
   }
 
