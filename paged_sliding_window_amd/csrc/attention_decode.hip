@@ -195,18 +195,6 @@ template <int N>
 __device__ __forceinline__ void lds_wait(bf16x4& a, bf16x4& b) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N < 15 ? N : 15));
 }
-// max / sum of the values of lanes l and l ^ 32, in every lane (one
-// v_permlane32_swap instead of an LDS permute); both lanes of a pair get the
-// same, order-independent result.
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // A vector load the compiler does not track (so it adds no vmcnt(0) waits of
 // its own around the LDS-DMA pipeline): the result may be used only after
 // vm_wait_tied<N>(), which waits until at most N vector-memory operations of

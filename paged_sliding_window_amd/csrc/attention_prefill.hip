@@ -44,9 +44,11 @@
 
 namespace psw {
 
-template <int D>
+template <int D, int WAVES, int STAGES>
 struct PrefillShape {
-  static constexpr int kWaves = 4;
+  static constexpr int kD = D;
+  static constexpr int kWaves = WAVES;
+  static constexpr int kStages = STAGES;  // tile buffers in the LDS ring
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kRowsPerWave = 32;
   static constexpr int kBlockM = kWaves * kRowsPerWave;
@@ -60,17 +62,22 @@ struct PrefillShape {
   static constexpr int kRowsPerInstr = 1024 / (D * 2);
   static constexpr int kInstrPerTile = kTile / kRowsPerInstr;
   static constexpr int kInstrPerWave = kInstrPerTile / kWaves;
+  static constexpr int kVmPerTile = 2 * kInstrPerWave;  // vector-memory ops per wave per tile
   static constexpr int kKBlock = 1024 + 16;
   static constexpr int kVBlock = 1024 + 64;
   static constexpr int kKBytes = kInstrPerTile * kKBlock;
   static constexpr int kVBytes = kInstrPerTile * kVBlock;
   static constexpr int kBufBytes = kKBytes + kVBytes;
+  static constexpr int kLdsBytes = kStages * kBufBytes;
   static constexpr int kQFrags = D / 16;   // MFMA k-steps of the score product
   static constexpr int kOBlocks = D / 32;  // 32-column output blocks
   static constexpr int kPvSteps = 2 * kOBlocks;
-  static_assert(kRowsPerInstr * D * 2 == 1024 && kInstrPerWave * kWaves == kInstrPerTile,
+  static_assert(kRowsPerInstr * D * 2 == 1024 && kInstrPerWave >= 1 &&
+                    kInstrPerWave * kWaves == kInstrPerTile,
                 "tile rows must split evenly into LDS-DMA instructions and waves");
-  static_assert(2 * kBufBytes <= 80 * 1024, "two workgroups must fit in one CU's LDS");
+  static_assert(kStages >= 2 && kStages <= 4, "LDS ring depth");
+  // two waves per SIMD: one workgroup of 8 waves or two of 4 per CU (160 KB LDS)
+  static_assert(kLdsBytes * (8 / kWaves) <= 160 * 1024, "LDS of the resident workgroups");
 };
 
 // Byte offset of tile row r inside a K or V tile buffer.
@@ -125,10 +132,10 @@ __device__ __forceinline__ float dot2_bf16(bf16x2 a, bf16x2 b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
 }
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void
+template <class S>
+__global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
 prefill_attention_kernel(const AttnParams p) {
-  using S = PrefillShape<D>;
+  constexpr int D = S::kD;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
@@ -211,6 +218,10 @@ prefill_attention_kernel(const AttnParams p) {
       if (row_valid) qf[c] = *reinterpret_cast<const bf16x8*>(qrow + c * 16);
       else qf[c] = bf16x8{};
     }
+    // Q has landed before any tile load is issued: otherwise the compiler
+    // guards the first use of Q inside the tile loop with a wait for every
+    // outstanding load, which would drain the tile prefetch on each iteration
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   }
 
   f32x16 o[S::kOBlocks];
@@ -242,13 +253,32 @@ prefill_attention_kernel(const AttnParams p) {
     const bool lane_second = two_segs && rq >= 16;
     const uint32_t lane_off = (uint32_t)(((two_segs ? (rq & 15) : rq) * pitch) + dma_ch * 16);
 
-    // Block-table entries of a tile's keys first (lane 0) and first + 16 (lane
-    // 1), read with a vector load one tile ahead: it is counted by vmcnt like
-    // the tile loads (the loop waits for both at its top), whereas a scalar
-    // load would share lgkmcnt with the LDS reads and stall their pipelines.
-    auto load_blocks = [&](int tile) __attribute__((always_inline)) -> int {
-      const int key = min(tile * S::kTile + (lane & 1) * 16, seq_len - 1);
-      return bt[key >> bs_log2];
+    // Block-table entries of the workgroup's tiles live in two registers:
+    // lane l of ent0 / ent1 holds the entry of block blk0 + l / blk0 + 64 + l
+    // (clamped to the request's last block), read before the tile loop, so the
+    // loop issues no table loads of its own.  A tile whose blocks fall outside
+    // the 128 held entries reloads the window (its use waits for every
+    // outstanding load; only tile ranges longer than 128 blocks get there).
+    const int last_blk = (seq_len - 1) >> bs_log2;
+    int blk0 = 0, ent0 = 0, ent1 = 0;
+    // The two loads and their wait are one assembly block: the compiler does
+    // not track them, so it adds no wait of its own where the entries are
+    // read (which would also wait for the tile loads in flight).
+    auto load_window = [&](int b) __attribute__((always_inline)) {
+      blk0 = b;
+      const int32_t* a0 = bt + min(b + lane, last_blk);
+      const int32_t* a1 = bt + min(b + 64 + lane, last_blk);
+      asm volatile(
+          "global_load_dword %0, %2, off\n\t"
+          "global_load_dword %1, %3, off\n\t"
+          "s_waitcnt vmcnt(0)"
+          : "=&v"(ent0), "=&v"(ent1)
+          : "v"(a0), "v"(a1)
+          : "memory");
+    };
+    auto entry = [&](int rel) __attribute__((always_inline)) -> int {
+      return rel < 64 ? __builtin_amdgcn_readlane(ent0, rel)
+                      : __builtin_amdgcn_readlane(ent1, rel - 64);
     };
     // Fast path of a tile's DMA: every instruction is a scalar base (lo) plus
     // one 32-bit offset per lane (voff).
@@ -257,17 +287,23 @@ prefill_attention_kernel(const AttnParams p) {
       uint32_t voff;
       bool fast;
     };
-    auto plan_tile = [&](int tile, int blocks) __attribute__((always_inline)) {
-      const int b0 = __builtin_amdgcn_readlane(blocks, 0);
-      const int b1 = two_segs ? __builtin_amdgcn_readlane(blocks, 1) : b0;
+    auto plan_tile = [&](int tile) __attribute__((always_inline)) {
+      DmaPlan d;
+      d.fast = false;
+      if (!fast_blocks) return d;
       const int first = tile * S::kTile;
+      // with 16-key blocks keys [first, first + 16) sit in block b and the
+      // rest in b + 1; larger blocks hold the whole tile
+      const int b = first >> bs_log2;
+      if (b < blk0 || b + 1 - blk0 >= 128) load_window(b);
+      const int b0 = entry(b - blk0);
+      const int b1 = two_segs ? entry(b + 1 - blk0) : b0;
       // byte offsets of the two segments in the cache (first row of each)
       const int64_t seg0 = (((int64_t)b0 << bs_log2) + (first & bs_mask)) * pitch;
       const int64_t seg1 = ((int64_t)b1 << bs_log2) * pitch;
-      DmaPlan d;
       d.lo = two_segs ? min(seg0, seg1) : seg0;
       const int64_t delta = two_segs ? max(seg0, seg1) - d.lo : 0;
-      d.fast = fast_blocks && first + S::kTile <= seq_len && delta < ((int64_t)1 << 31);
+      d.fast = first + S::kTile <= seq_len && delta < ((int64_t)1 << 31);
       const bool lane_far = lane_second ? seg1 > seg0 : seg0 > seg1;
       d.voff = lane_off + (lane_far ? (uint32_t)delta : 0u);
       return d;
@@ -321,33 +357,42 @@ prefill_attention_kernel(const AttnParams p) {
     const uint32_t smem0 = lds_addr(smem);
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // Pipeline: the block-table entries of tile u are read in iteration u - 3,
-    // its DMA plan is computed between the output MFMAs of iteration u - 2 (in
-    // their shadow), and its DMA is issued in iteration u - 1.
-    issue_tile(t_lo, 0, plan_tile(t_lo, load_blocks(t_lo)));
-    DmaPlan nd;  // plan of tile t + 1
+    // Pipeline over a ring of NS tile buffers: the DMA plan of tile u is made
+    // in iteration u - NS (after its output MFMAs are issued) and its DMA is
+    // issued in iteration u - NS + 1, spread over the score MFMAs, so up to
+    // NS - 1 tiles are in flight while one is computed.
+    constexpr int NS = S::kStages;
+    if (fast_blocks) load_window((t_lo * S::kTile) >> bs_log2);
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j)
+      if (t_lo + j < t_hi) issue_tile(t_lo + j, j, plan_tile(t_lo + j));
+    DmaPlan nd;  // plan of tile t + NS - 1
     nd.fast = false;
-    if (t_lo + 1 < t_hi) nd = plan_tile(t_lo + 1, load_blocks(t_lo + 1));
-    int blk_next = t_lo + 2 < t_hi ? load_blocks(t_lo + 2) : 0;  // entries of tile t + 2
+    if (t_lo + NS - 1 < t_hi) nd = plan_tile(t_lo + NS - 1);
 
-    for (int t = t_lo; t < t_hi; ++t) {
-      const int buf = (t - t_lo) & 1;
-      // this wave's LDS-DMA loads of tile t have landed; the barrier extends
-      // that to every wave and fences the reads of the other buffer (tile t-1)
-      // before it is refilled
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    int buf = 0;  // (t - t_lo) % NS
+    for (int t = t_lo; t < t_hi; ++t, buf = buf + 1 == NS ? 0 : buf + 1) {
+      // this wave's LDS-DMA loads of tile t have landed once at most the loads
+      // of the tiles issued after it (up to NS - 2, kVmPerTile each, more on
+      // the per-lane path) are outstanding; the barrier extends that to every
+      // wave and fences the reads of tile t - 1's buffer before it is refilled
+      const int later = min(NS - 2, t_hi - 1 - t);
+      if (NS >= 4 && later >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * S::kVmPerTile));
+      else if (NS >= 3 && later >= 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(S::kVmPerTile));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       lds_barrier();
       const int base = t * S::kTile;
       const bool skip = base > any_hi || base + S::kTile - 1 < any_lo;  // no row of the wave sees it
-      // The fast-path DMA of tile t + 1 is spread over the score MFMAs below
-      // (all waves issuing right after the barrier stall on the shared address
-      // unit); the other cases issue it here.
-      const int blk_after = t + 3 < t_hi ? load_blocks(t + 3) : 0;  // entries of tile t + 3
-      if (t + 1 < t_hi && (!nd.fast || skip)) issue_tile(t + 1, buf ^ 1, nd);
-      const bool inter = t + 1 < t_hi && nd.fast;
+      // Tile tn goes to the buffer tile t - 1 used.  The fast-path DMA is
+      // spread over the score MFMAs below (all waves issuing right after the
+      // barrier stall on the shared address unit); the other cases issue it
+      // here.
+      const int tn = t + NS - 1;
+      const int bn = buf == 0 ? NS - 1 : buf - 1;
+      if (tn < t_hi && (!nd.fast || skip)) issue_tile(tn, bn, nd);
+      const bool inter = tn < t_hi && nd.fast;
       if (skip) {
-        if (t + 2 < t_hi) nd = plan_tile(t + 2, blk_next);
-        blk_next = blk_after;
+        if (tn + 1 < t_hi) nd = plan_tile(tn + 1);
         continue;
       }
       const uint32_t kt = smem0 + (uint32_t)(buf * S::kBufBytes);
@@ -371,9 +416,9 @@ prefill_attention_kernel(const AttnParams p) {
           if constexpr (c + KA < N) kf[(c + KA) % (KA + 1)] = lds_read_b128_at<(c + KA) * 32>(ka);
           constexpr int step = N / S::kInstrPerWave;
           if constexpr (c % step == 0) {
-            if (inter) dma_k(nd, buf ^ 1, c / step);
+            if (inter) dma_k(nd, bn, c / step);
           } else if constexpr (c % step == step / 2) {
-            if (inter) dma_v(nd, buf ^ 1, c / step);
+            if (inter) dma_v(nd, bn, c / step);
           }
         });
       }
@@ -387,7 +432,7 @@ prefill_attention_kernel(const AttnParams p) {
       float mx = s[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-      mx = fmaxf(mx, swap_halves(mx)) * c2;
+      mx = pair_max(mx) * c2;
       // move the running max only when it grows by more than 2^8
       if (__ballot(mx > m_run + 8.f) != 0) {
         const float m_new = fmaxf(m_run, mx);
@@ -430,16 +475,14 @@ prefill_attention_kernel(const AttnParams p) {
           o[st % S::kOBlocks] = mfma32(cat8(vr[st % (VA + 1)][0], vr[st % (VA + 1)][1]),
                                        st / S::kOBlocks == 0 ? pf0 : pf1, o[st % S::kOBlocks]);
           if constexpr (st + VA < N) read_v(std::integral_constant<int, st + VA>{});
-          // (unused when t + 2 >= t_hi: no branch inside the MFMA sequence)
-          if constexpr (st == 1) nd = plan_tile(t + 2, blk_next);
         });
       }
-      blk_next = blk_after;
+      if (tn + 1 < t_hi) nd = plan_tile(tn + 1);  // in the shadow of the last MFMAs
     }
   }
 
   // ---- epilogue ------------------------------------------------------------
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (row_valid) {
     const int64_t orow = ((int64_t)split * p.num_tokens + token) * p.num_q_heads + head;
@@ -473,14 +516,23 @@ bool prefill_supported(int head_dim_qk, int head_dim_v, int queries_per_kv, bool
          (head_dim_qk == 64 || head_dim_qk == 128 || head_dim_qk == 256);
 }
 
+// Launch shapes: two 4-wave workgroups per CU, two tile buffers each.  One
+// 8-wave workgroup per CU with a four-deep ring (prefetch distance three
+// tiles) measured no faster on the 16,550-token workload: the tile loads are
+// not what the loop waits for.
+template <int D> struct PrefillConfig;
+template <> struct PrefillConfig<64> { using S = PrefillShape<64, 4, 2>; };
+template <> struct PrefillConfig<128> { using S = PrefillShape<128, 4, 2>; };
+template <> struct PrefillConfig<256> { using S = PrefillShape<256, 4, 2>; };
+
 template <int D>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
-  using S = PrefillShape<D>;
+  using S = typename PrefillConfig<D>::S;
   const int block_q = S::kBlockM / p.queries_per_kv;
   const int gx = p.num_tokens / block_q + p.num_seqs;
   if (gx == 0) return hipSuccess;
-  const size_t lds = 2 * (size_t)S::kBufBytes;
-  auto kern = prefill_attention_kernel<D>;
+  const size_t lds = S::kLdsBytes;
+  auto kern = prefill_attention_kernel<S>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;

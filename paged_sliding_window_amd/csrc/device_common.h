@@ -132,6 +132,20 @@ __device__ __forceinline__ float swap_halves(float x) {  // value of lane l ^ 32
   return __shfl_xor(x, 32, kWave);
 }
 
+// max / sum of the values of lanes l and l ^ 32, in every lane, with one
+// v_permlane32_swap (a VALU instruction) instead of an LDS permute.  The swap
+// leaves the low half's value in one register and the high half's in the
+// other in both halves, so both lanes of a pair get the same result, added in
+// the same order.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
   return x;

@@ -55,7 +55,9 @@ def _check_workload(w, T, block_q, qpk):
 def test_every_query_block_of_the_workloads(cfg):
     w = make_config(cfg)
     qpk = w.num_q_heads // w.num_kv_heads
-    _check_workload(w, 64, 128 // qpk, qpk)   # the prefill kernel's tiling
+    for block_m in (128, 256):                # the prefill kernel's tilings (32-key tiles)
+        _check_workload(w, 32, block_m // qpk, qpk)
+    _check_workload(w, 64, 128 // qpk, qpk)
     _check_workload(w, 32, 8, qpk)            # the pages' test tiling
 
 
