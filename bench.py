@@ -99,7 +99,8 @@ def cpu_baseline(w):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_attention_gemma16550_traffic.json")
-PREFILL_SOURCES = ["attention_prefill.hip", "device_common.h", "mask_bounds.h", "psw_internal.h"]
+PREFILL_SOURCES = ["attention_prefill.hip", "asm_ops.h", "device_common.h", "mask_bounds.h",
+                   "psw_internal.h"]
 
 
 def measured_traffic():
@@ -209,7 +210,7 @@ def main():
             "step": "slot_mapping + kv_cache_write + swa_mm_attention",
         },
         "roofline": {
-            "kernel": "prefill_attention_kernel<256,256>",
+            "kernel": "prefill_attention_kernel<PrefillShape<256, 4, 2>>",
             "bound": "mfma",
             "achieved": round(achieved, 3),
             "peak": MFMA_BF16_PEAK_TFLOPS,

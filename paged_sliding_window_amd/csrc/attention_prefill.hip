@@ -39,6 +39,7 @@
 //     allowed keys form one interval).
 #include <utility>
 
+#include "asm_ops.h"
 #include "device_common.h"
 #include "psw_internal.h"
 
@@ -90,42 +91,6 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(
       (const __attribute__((address_space(1))) void*)gsrc,
       (__attribute__((address_space(3))) void*)(lds_void*)lds_dst, 16, 0, 0);
-}
-
-// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1.
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// LDS reads the compiler does not track (see lds_read_tr4_async): the result
-// may be consumed only after lds_wait<N>() on it.
-template <int OFF>
-__device__ __forceinline__ bf16x8 lds_read_b128_at(uint32_t addr) {
-  bf16x8 r;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-  return r;
-}
-template <int OFF>
-__device__ __forceinline__ bf16x4 lds_read_tr4_at(uint32_t addr) {
-  i16x4 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-  return __builtin_bit_cast(bf16x4, r);
-}
-// Wait until at most N LDS operations of this wave are outstanding (they
-// complete in issue order; outstanding scalar loads only make the wait longer)
-// and tie the given registers to that point.
-template <int N>
-__device__ __forceinline__ void lds_wait(bf16x8& a) {
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N < 15 ? N : 15));
-}
-template <int N>
-__device__ __forceinline__ void lds_wait(bf16x4& a, bf16x4& b) {
-  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N < 15 ? N : 15));
 }
 
 __device__ __forceinline__ float dot2_bf16(bf16x2 a, bf16x2 b, float c) {
