@@ -5,8 +5,8 @@ multimodal prefill (16,550 tokens, 60 images of 256 tokens, W 1024, 16 query /
 8 KV heads, head dim 256, paged in blocks of 16):
   slot mapping of the new tokens -> KV-cache write -> paged prefill attention.
 The decode half of the path (MLA-shaped split-KV decode: 64 requests, 128 heads,
-576/512 latent, 8 history splits + the current key, LSE combine) is timed in
-the same run and reported under "decode".
+576/512 latent, history partial(s) + the current key's partial from one call,
+LSE combine) is timed in the same run and reported under "decode".
 
 Reported value: algorithmic TFLOP/s = 4 * head_dim FLOP per allowed
 (query, key, head) triple, 3.0115e11 per step, over the measured step time.
@@ -302,23 +302,23 @@ def bench_decode(args, torch, psw, np):
                        cache, None)
     new_rows = bits_to_bf16(np.stack([k[-1] for k in w.k_bits]))
     del slots_ctx
-    kr_hist = i32(w.key_ranges)
-    kr_cur = i32(w.current_ranges)
+    # the history splits and the current key are the key ranges of ONE call: it
+    # emits S + 1 partials (each with its LSE), S history pieces and the current
+    # key's partial last, which lse_combine then merges
     S = w.key_ranges.shape[0]
+    kr_all = i32(np.concatenate([w.key_ranges, w.current_ranges], axis=0))
+    P = S + 1
     pdt = torch.float32 if args.decode_partials == "f32" else torch.bfloat16
-    hist_o = torch.empty((S, R, H, DV), dtype=pdt, device="cuda")
-    hist_l = torch.empty((S, R, H), dtype=torch.float32, device="cuda")
-    cur_o = torch.empty((1, R, H, DV), dtype=pdt, device="cuda")
-    cur_l = torch.empty((1, R, H), dtype=torch.float32, device="cuda")
+    part_o = torch.empty((P, R, H, DV), dtype=pdt, device="cuda")
+    part_l = torch.empty((P, R, H), dtype=torch.float32, device="cuda")
     out = torch.empty((R * H, DV), dtype=torch.bfloat16, device="cuda")
     slots = torch.empty(R, dtype=torch.int32, device="cuda")
-    outs = [hist_o[j].view(R * H, DV) for j in range(S)] + [cur_o[0].view(R * H, DV)]
-    lses = [hist_l[j].view(R * H) for j in range(S)] + [cur_l[0].view(R * H)]
-    # one workspace for both attention calls (they run in order on one stream)
+    outs = [part_o[j].view(R * H, DV) for j in range(P)]
+    lses = [part_l[j].view(R * H) for j in range(P)]
     ws_args = psw.ops._attn_args(q, cache, None, bt, qsl, seq_lens, scale=w.scale, window=0,
                                  causal=True, chunk_size=0, chunk_lookback=-1, mm_ranges=None,
-                                 key_ranges=kr_hist, out=hist_o, lse=hist_l, head_dim_v=DV,
-                                 out_dtype=0, num_splits=S)
+                                 key_ranges=kr_all, out=part_o, lse=part_l, head_dim_v=DV,
+                                 out_dtype=0, num_splits=P)
     ws = torch.empty(max(1, psw.ops.attention_workspace_size(ws_args)), dtype=torch.uint8,
                      device="cuda")
     steps = max(args.steps, 10)
@@ -330,11 +330,8 @@ def bench_decode(args, torch, psw, np):
         if i is not None:
             ev[i][0].record()
         psw.swa_mm_attention(q, cache, None, bt, qsl, seq_lens, scale=w.scale, window=0,
-                             causal=True, key_ranges=kr_hist, head_dim_v=DV, out=hist_o,
-                             lse=hist_l, out_dtype=pdt, workspace=ws)
-        psw.swa_mm_attention(q, cache, None, bt, qsl, seq_lens, scale=w.scale, window=0,
-                             causal=True, key_ranges=kr_cur, head_dim_v=DV, out=cur_o,
-                             lse=cur_l, out_dtype=pdt, workspace=ws)
+                             causal=True, key_ranges=kr_all, head_dim_v=DV, out=part_o,
+                             lse=part_l, out_dtype=pdt, workspace=ws)
         if i is not None:
             ev[i][1].record()
         psw.lse_combine(outs, lses, out=out)
@@ -370,8 +367,10 @@ def bench_decode(args, torch, psw, np):
         "attention_GBps": round(attn_gbs, 1),
         "combine_ms": round(comb_ms, 5),
         "history_splits": S,
+        "partials": P,
         "partial_dtype": args.decode_partials,
-        "step": "slot_mapping + kv_cache_write + history and current partials + lse_combine",
+        "step": "slot_mapping + kv_cache_write + history and current partials (one call) "
+                "+ lse_combine",
     }
 
 
