@@ -17,7 +17,7 @@ the pages' definitions:
 Every function is pinned by tests that do not re-derive it (printed values,
 closed forms, textbook reductions, brute force); none is "parity unpinned".
 """
-from .slot_mapping import slot_mapping_ref  # noqa: F401
+from .slot_mapping import slot_mapping_cp_ref, slot_mapping_ref  # noqa: F401
 from .mask import allowed_ref, allowed_rows, row_interval_ref  # noqa: F401
 from .tile_bounds import tile_bounds_ref  # noqa: F401
 from .attention import attention_ref, attention_pruned_ref  # noqa: F401
