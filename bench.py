@@ -274,9 +274,41 @@ def bench_slot_mapping(torch, psw, np, num_reqs=4096, seed=7):
     ms = e0.elapsed_time(e1) / reps
     alg = n * 12 + int(need.sum()) * 4 + (m - n) * 4
     gbs = alg / (ms * 1e-3) / 1e9
-    return {"tokens": n, "max_num_tokens": m, "requests": num_reqs, "block_size": B,
-            "ms": round(ms, 5), "algorithmic_bytes": alg, "GBps": round(gbs, 1),
-            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    res = {"tokens": n, "max_num_tokens": m, "requests": num_reqs, "block_size": B,
+           "ms": round(ms, 5), "algorithmic_bytes": alg, "GBps": round(gbs, 1),
+           "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+    # the same batch on rank 3 of an 8-rank context-parallel group (interleave 16,
+    # 64-token KV blocks): each rank's table holds only its own logical blocks
+    world, rank, inter, kvb = 8, 3, 16, 64
+    need_cp = -(-lens // (kvb * world)) * (kvb // B)
+    bt_cp = np.full((num_reqs, int(need_cp.max())), -1, dtype=np.int32)
+    perm = rng.permutation(int(need_cp.sum())).astype(np.int32)
+    off = 0
+    for r in range(num_reqs):
+        bt_cp[r, :need_cp[r]] = perm[off:off + need_cp[r]]
+        off += need_cp[r]
+    d_bt_cp = i32(bt_cp)
+
+    def run_cp():
+        psw.slot_mapping_cp(d_qsl, d_pos, d_bt_cp, B, m, kv_cache_block_size=kvb,
+                            cp_world_size=world, cp_rank=rank, cp_interleave=inter, out=out)
+    for _ in range(3):
+        run_cp()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        run_cp()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_cp = e0.elapsed_time(e1) / reps
+    alg_cp = n * 12 + int(need_cp.sum()) * 4 + (m - n) * 4
+    gbs_cp = alg_cp / (ms_cp * 1e-3) / 1e9
+    res["context_parallel_rank"] = {
+        "cp_world_size": world, "cp_rank": rank, "cp_interleave": inter,
+        "kv_cache_block_size": kvb, "ms": round(ms_cp, 5), "algorithmic_bytes": alg_cp,
+        "GBps": round(gbs_cp, 1), "frac_of_hbm_peak": round(gbs_cp / HBM_PEAK_GBS, 4)}
+    return res
 
 
 def bench_decode(args, torch, psw, np):

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define PSW_ABI_VERSION 2
+#define PSW_ABI_VERSION 3
 
 enum psw_status {
   PSW_OK = 0,
@@ -73,6 +73,43 @@ int psw_slot_mapping(const int32_t* query_start_loc, int32_t num_reqs,
                      const int32_t* block_table, int32_t block_table_stride,
                      int32_t block_size, int32_t* slot_mapping, int32_t max_num_tokens,
                      void* stream);
+
+/*
+ * psw_slot_mapping_cp - [SLOT] section 3.1 (steps 1-5 of the context-parallel
+ * interleave), section 2.2 (circular cache) and section 4.2 (parameters).
+ * The slot mapping of ONE context-parallel rank: with V = kv_cache_block_size *
+ * cp_world_size, a token at position pos >= 0 of request r belongs to rank
+ *     ((pos % V) / cp_interleave) % cp_world_size
+ * and, on its own rank, gets
+ *     local   = ((pos % V) / (cp_world_size * cp_interleave)) * cp_interleave
+ *               + (pos % V) % cp_interleave
+ *     logical = (pos / V) * (kv_cache_block_size / block_size) + local / block_size
+ *     slot    = block_table[r * block_table_stride + logical] * block_size
+ *               + local % block_size
+ * while tokens owned by another rank get -1.  With circular = 1 (a circular
+ * cache; the page allows it only without context parallelism) every position
+ * uses logical block 0 and offset pos % block_size.  As in psw_slot_mapping: a
+ * negative position (or one of 2^31 and above), a logical block
+ * >= block_table_stride or a negative table entry gives -1, and
+ * [num_tokens, max_num_tokens) is filled with -1.  cp_world_size = 1 is exactly
+ * psw_slot_mapping.
+ *   query_start_loc, positions, block_table, slot_mapping: as psw_slot_mapping (device)
+ *   kv_cache_block_size  tokens per physical KV block, a multiple of block_size
+ *   cp_world_size, cp_rank  ranks of the context-parallel group and this rank
+ *   cp_interleave        tokens per interleave segment, dividing kv_cache_block_size
+ * Errors: PSW_ERR_INVALID as psw_slot_mapping, and if kv_cache_block_size is not a
+ * positive multiple of block_size, cp_world_size < 1, cp_rank outside
+ * [0, cp_world_size), cp_interleave < 1 or not a divisor of kv_cache_block_size,
+ * kv_cache_block_size * cp_world_size >= 2^31, circular not 0 or 1, or circular
+ * with cp_world_size > 1.
+ */
+int psw_slot_mapping_cp(const int32_t* query_start_loc, int32_t num_reqs,
+                        const int64_t* positions, int32_t num_tokens,
+                        const int32_t* block_table, int32_t block_table_stride,
+                        int32_t block_size, int32_t kv_cache_block_size,
+                        int32_t cp_world_size, int32_t cp_rank, int32_t cp_interleave,
+                        int32_t circular, int32_t* slot_mapping, int32_t max_num_tokens,
+                        void* stream);
 
 /*
  * psw_kv_cache_write - [SLOT] section 1 (the slot id addresses a token's K/V

@@ -9,6 +9,7 @@ from .ops import (  # noqa: F401
     kv_cache_write,
     lse_combine,
     slot_mapping,
+    slot_mapping_cp,
     swa_mm_attention,
     tile_bounds,
 )

@@ -48,6 +48,8 @@ EXPORTS = {
     "psw_status_string": (ctypes.c_char_p, [_i32]),
     "psw_last_error": (ctypes.c_char_p, []),
     "psw_slot_mapping": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _i32, _vp]),
+    "psw_slot_mapping_cp": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                   _i32, _vp, _i32, _vp]),
     "psw_kv_cache_write": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _vp]),
     "psw_swa_mm_attention": (_i32, [ctypes.POINTER(PswAttnArgs), _vp]),
     "psw_attention_workspace_size": (_i32, [ctypes.POINTER(PswAttnArgs), ctypes.POINTER(_i64)]),

@@ -82,6 +82,51 @@ int psw_slot_mapping(const int32_t* query_start_loc, int32_t num_reqs, const int
                    "slot_mapping");
 }
 
+int psw_slot_mapping_cp(const int32_t* query_start_loc, int32_t num_reqs,
+                        const int64_t* positions, int32_t num_tokens,
+                        const int32_t* block_table, int32_t block_table_stride,
+                        int32_t block_size, int32_t kv_cache_block_size,
+                        int32_t cp_world_size, int32_t cp_rank, int32_t cp_interleave,
+                        int32_t circular, int32_t* slot_mapping, int32_t max_num_tokens,
+                        void* stream) {
+  if (num_reqs < 0 || num_tokens < 0)
+    return fail(PSW_ERR_INVALID, "num_reqs (%d) and num_tokens (%d) must be >= 0", num_reqs,
+                num_tokens);
+  if (block_table_stride < 1 || block_size < 1)
+    return fail(PSW_ERR_INVALID, "block_table_stride (%d) and block_size (%d) must be >= 1",
+                block_table_stride, block_size);
+  if (kv_cache_block_size < 1 || kv_cache_block_size % block_size != 0)
+    return fail(PSW_ERR_INVALID, "kv_cache_block_size (%d) must be a positive multiple of "
+                "block_size (%d)", kv_cache_block_size, block_size);
+  if (cp_world_size < 1 || cp_rank < 0 || cp_rank >= cp_world_size)
+    return fail(PSW_ERR_INVALID, "cp_rank (%d) must lie in [0, cp_world_size = %d)", cp_rank,
+                cp_world_size);
+  if (cp_interleave < 1 || kv_cache_block_size % cp_interleave != 0)
+    return fail(PSW_ERR_INVALID, "cp_interleave (%d) must divide kv_cache_block_size (%d)",
+                cp_interleave, kv_cache_block_size);
+  if ((int64_t)kv_cache_block_size * cp_world_size >= ((int64_t)1 << 31))
+    return fail(PSW_ERR_INVALID, "kv_cache_block_size * cp_world_size must be below 2^31");
+  if (circular != 0 && circular != 1)
+    return fail(PSW_ERR_INVALID, "circular must be 0 or 1, got %d", circular);
+  if (circular && cp_world_size != 1)
+    return fail(PSW_ERR_INVALID, "a circular cache is not allowed with cp_world_size %d > 1",
+                cp_world_size);
+  if (max_num_tokens < num_tokens)
+    return fail(PSW_ERR_INVALID, "max_num_tokens (%d) < num_tokens (%d)", max_num_tokens,
+                num_tokens);
+  if (max_num_tokens > 0 && slot_mapping == nullptr)
+    return fail(PSW_ERR_INVALID, "slot_mapping is NULL");
+  if (num_tokens > 0 && (positions == nullptr || query_start_loc == nullptr ||
+                         (num_reqs > 0 && block_table == nullptr)))
+    return fail(PSW_ERR_INVALID, "query_start_loc, positions and block_table are required");
+  return check_hip(psw::launch_slot_mapping_cp(query_start_loc, num_reqs, positions, num_tokens,
+                                               block_table, block_table_stride, block_size,
+                                               kv_cache_block_size, cp_world_size, cp_rank,
+                                               cp_interleave, circular != 0, slot_mapping,
+                                               max_num_tokens, (hipStream_t)stream),
+                   "slot_mapping_cp");
+}
+
 int psw_kv_cache_write(const void* k_new, const void* v_new, const int32_t* slot_mapping,
                        int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim_k,
                        int32_t head_dim_v, void* k_cache, void* v_cache, int64_t num_slots,

@@ -32,6 +32,13 @@ hipError_t launch_slot_mapping(const int32_t* qsl, int num_reqs, const int64_t* 
                                int block_size, int32_t* out, int max_num_tokens,
                                hipStream_t stream);
 
+// Context-parallel rank / circular-cache variant (geometry validated by the caller).
+hipError_t launch_slot_mapping_cp(const int32_t* qsl, int num_reqs, const int64_t* positions,
+                                  int num_tokens, const int32_t* block_table, int stride,
+                                  int block_size, int kv_cache_block_size, int cp_world_size,
+                                  int cp_rank, int cp_interleave, bool circular, int32_t* out,
+                                  int max_num_tokens, hipStream_t stream);
+
 hipError_t launch_kv_cache_write(const uint16_t* k_new, const uint16_t* v_new,
                                  const int32_t* slots, int num_tokens, int num_kv_heads,
                                  int head_dim_k, int head_dim_v, uint16_t* k_cache,

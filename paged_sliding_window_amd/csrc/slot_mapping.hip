@@ -10,6 +10,8 @@
 // with 16-byte stores, so every wave streams contiguous positions and slots.
 // Block-table entries are read per token; consecutive tokens of a request hit
 // the same cache line, which plays the role of the page's bounded window.
+#include <type_traits>
+
 #include "psw_internal.h"
 
 namespace psw {
@@ -41,10 +43,59 @@ __device__ __forceinline__ int find_request_wave(const int32_t* __restrict__ qsl
   return lo;
 }
 
+// Geometry of the context-parallel and circular modes ([SLOT] sections 2.2,
+// 3.1 and 4.2), validated on the host.  pow2: every size below is a power of
+// two and the *_log2 fields hold their logarithms (shifts and masks instead
+// of divisions).
+struct SlotGeom {
+  int block_size, kv_block, blocks_per_kv, world, rank, inter;
+  int pow2, bs_log2, kvb_log2, world_log2, inter_log2, bpk_log2;
+};
+
+enum SlotMode { kSlotPlain = 0, kSlotCp = 1, kSlotCircular = 2 };
+
+// Logical block and offset of position p (p >= 0, below 2^31) on this rank:
+// false when another rank owns it.
+template <int MODE, bool POW2>
+__device__ __forceinline__ bool cp_place(uint32_t p, const SlotGeom& g, uint32_t& lb,
+                                         uint32_t& off) {
+  if constexpr (MODE == kSlotCircular) {
+    // the circular cache keeps every position in logical block 0
+    lb = 0;
+    off = POW2 ? (p & (uint32_t)(g.block_size - 1)) : p % (uint32_t)g.block_size;
+    return true;
+  } else if constexpr (POW2) {
+    // step 1: virtual block of the world's physical blocks
+    const int vbs_log2 = g.kvb_log2 + g.world_log2;
+    const uint32_t vb = p >> vbs_log2, vo = p & ((1u << vbs_log2) - 1u);
+    // step 2: owner of the position's interleave segment
+    if (((vo >> g.inter_log2) & (uint32_t)(g.world - 1)) != (uint32_t)g.rank) return false;
+    // step 3: this rank's segments of the virtual block, end to end
+    const uint32_t local = ((vo >> (g.world_log2 + g.inter_log2)) << g.inter_log2) |
+                           (vo & (uint32_t)(g.inter - 1));
+    // step 4: logical block and offset
+    lb = (vb << g.bpk_log2) + (local >> g.bs_log2);
+    off = local & (uint32_t)(g.block_size - 1);
+    return true;
+  } else {
+    const uint32_t vbs = (uint32_t)g.kv_block * (uint32_t)g.world;
+    const uint32_t vb = p / vbs, vo = p - vb * vbs;
+    const uint32_t seg = vo / (uint32_t)g.inter;
+    if (seg % (uint32_t)g.world != (uint32_t)g.rank) return false;
+    const uint32_t wi = (uint32_t)g.world * (uint32_t)g.inter;
+    const uint32_t local = (vo / wi) * (uint32_t)g.inter + (vo - seg * (uint32_t)g.inter);
+    const uint32_t lbl = local / (uint32_t)g.block_size;
+    lb = vb * (uint32_t)g.blocks_per_kv + lbl;
+    off = local - lbl * (uint32_t)g.block_size;
+    return true;
+  }
+}
+
+template <int MODE, bool POW2>
 __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(
     const int32_t* __restrict__ qsl, int num_reqs, const int64_t* __restrict__ positions,
     int num_tokens, const int32_t* __restrict__ block_table, int stride, int block_size,
-    int32_t* __restrict__ out, int max_num_tokens) {
+    int32_t* __restrict__ out, int max_num_tokens, const SlotGeom g) {
   const int lane = threadIdx.x % kWaveLanes;
   const int64_t wave_t0 = ((int64_t)blockIdx.x * kSlotThreads + (threadIdx.x - lane)) *
                           kSlotTokensPerThread;
@@ -77,11 +128,21 @@ __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(
     if (t < num_tokens && num_reqs > 0) {
       while (r + 1 < num_reqs && qsl[r + 1] <= t) ++r;  // crossing into the next request
       const int64_t p = pos[j];
-      if (p >= 0) {
-        const int64_t lb = p / block_size;
-        if (lb < stride) {
+      if constexpr (MODE == kSlotPlain) {
+        if (p >= 0) {
+          const int64_t lb = p / block_size;
+          if (lb < stride) {
+            const int32_t b = block_table[(int64_t)r * stride + lb];
+            if (b >= 0) res[j] = (int32_t)(b * (int64_t)block_size + (p - lb * block_size));
+          }
+        }
+      } else {
+        uint32_t lb, off;
+        if (p >= 0 && p <= INT32_MAX && cp_place<MODE, POW2>((uint32_t)p, g, lb, off) &&
+            lb < (uint32_t)stride) {
+          // step 5: physical block through the table
           const int32_t b = block_table[(int64_t)r * stride + lb];
-          if (b >= 0) res[j] = (int32_t)(b * (int64_t)block_size + (p - lb * block_size));
+          if (b >= 0) res[j] = (int32_t)(b * (int64_t)block_size + off);
         }
       }
     }
@@ -98,17 +159,70 @@ __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(
   }
 }
 
+template <int MODE, bool POW2>
+static hipError_t launch_slot_t(const int32_t* qsl, int num_reqs, const int64_t* positions,
+                                int num_tokens, const int32_t* block_table, int stride,
+                                int block_size, int32_t* out, int max_num_tokens,
+                                const SlotGeom& g, hipStream_t stream) {
+  const int64_t threads = (max_num_tokens + kSlotTokensPerThread - 1) / kSlotTokensPerThread;
+  const int grid = (int)((threads + kSlotThreads - 1) / kSlotThreads);
+  hipLaunchKernelGGL((slot_mapping_kernel<MODE, POW2>), dim3(grid), dim3(kSlotThreads), 0, stream,
+                     qsl, num_reqs, positions, num_tokens, block_table, stride, block_size, out,
+                     max_num_tokens, g);
+  return hipGetLastError();
+}
+
 hipError_t launch_slot_mapping(const int32_t* qsl, int num_reqs, const int64_t* positions,
                                int num_tokens, const int32_t* block_table, int stride,
                                int block_size, int32_t* out, int max_num_tokens,
                                hipStream_t stream) {
   if (max_num_tokens == 0) return hipSuccess;
-  const int64_t threads = (max_num_tokens + kSlotTokensPerThread - 1) / kSlotTokensPerThread;
-  const int grid = (int)((threads + kSlotThreads - 1) / kSlotThreads);
-  hipLaunchKernelGGL(slot_mapping_kernel, dim3(grid), dim3(kSlotThreads), 0, stream, qsl,
-                     num_reqs, positions, num_tokens, block_table, stride, block_size, out,
-                     max_num_tokens);
-  return hipGetLastError();
+  SlotGeom g{};
+  return launch_slot_t<kSlotPlain, false>(qsl, num_reqs, positions, num_tokens, block_table,
+                                          stride, block_size, out, max_num_tokens, g, stream);
+}
+
+static int ilog2_exact(int v) {  // log2 of a power of two, else -1
+  if (v < 1 || (v & (v - 1)) != 0) return -1;
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+hipError_t launch_slot_mapping_cp(const int32_t* qsl, int num_reqs, const int64_t* positions,
+                                  int num_tokens, const int32_t* block_table, int stride,
+                                  int block_size, int kv_cache_block_size, int cp_world_size,
+                                  int cp_rank, int cp_interleave, bool circular, int32_t* out,
+                                  int max_num_tokens, hipStream_t stream) {
+  if (max_num_tokens == 0) return hipSuccess;
+  SlotGeom g{};
+  g.block_size = block_size;
+  g.kv_block = kv_cache_block_size;
+  g.blocks_per_kv = kv_cache_block_size / block_size;
+  g.world = cp_world_size;
+  g.rank = cp_rank;
+  g.inter = cp_interleave;
+  g.bs_log2 = ilog2_exact(block_size);
+  g.kvb_log2 = ilog2_exact(kv_cache_block_size);
+  g.world_log2 = ilog2_exact(cp_world_size);
+  g.inter_log2 = ilog2_exact(cp_interleave);
+  g.bpk_log2 = ilog2_exact(g.blocks_per_kv);
+  g.pow2 = g.bs_log2 >= 0 && g.kvb_log2 >= 0 && g.world_log2 >= 0 && g.inter_log2 >= 0 &&
+           g.bpk_log2 >= 0;
+  auto go = [&](auto mode, auto pow2) {
+    return launch_slot_t<decltype(mode)::value, decltype(pow2)::value>(
+        qsl, num_reqs, positions, num_tokens, block_table, stride, block_size, out,
+        max_num_tokens, g, stream);
+  };
+  using P = std::integral_constant<int, kSlotPlain>;
+  using C = std::integral_constant<int, kSlotCp>;
+  using R = std::integral_constant<int, kSlotCircular>;
+  using T = std::true_type;
+  using F = std::false_type;
+  if (circular) return g.bs_log2 >= 0 ? go(R{}, T{}) : go(R{}, F{});
+  // one rank: the interleave is the identity and the mapping is the plain one
+  if (cp_world_size == 1) return go(P{}, F{});
+  return g.pow2 ? go(C{}, T{}) : go(C{}, F{});
 }
 
 }  // namespace psw

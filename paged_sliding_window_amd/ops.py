@@ -50,6 +50,31 @@ def slot_mapping(query_start_loc: torch.Tensor, positions: torch.Tensor, block_t
     return out
 
 
+def slot_mapping_cp(query_start_loc: torch.Tensor, positions: torch.Tensor,
+                    block_table: torch.Tensor, block_size: int, max_num_tokens: int, *,
+                    kv_cache_block_size: Optional[int] = None, cp_world_size: int = 1,
+                    cp_rank: int = 0, cp_interleave: int = 1, circular: bool = False,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Slot mapping of one context-parallel rank, or of a circular cache
+    (psw_slot_mapping_cp); kv_cache_block_size defaults to block_size."""
+    _need(query_start_loc, "query_start_loc", torch.int32, 1)
+    _need(positions, "positions", torch.int64, 1)
+    _need(block_table, "block_table", torch.int32, 2)
+    if out is None:
+        out = torch.empty(max_num_tokens, dtype=torch.int32, device=positions.device)
+    _need(out, "out", torch.int32, 1)
+    if out.numel() < max_num_tokens:
+        raise ValueError("out is smaller than max_num_tokens")
+    kvb = block_size if kv_cache_block_size is None else kv_cache_block_size
+    check(load().psw_slot_mapping_cp(_ptr(query_start_loc), query_start_loc.numel() - 1,
+                                     _ptr(positions), positions.numel(), _ptr(block_table),
+                                     block_table.shape[1], int(block_size), int(kvb),
+                                     int(cp_world_size), int(cp_rank), int(cp_interleave),
+                                     int(bool(circular)), _ptr(out), int(max_num_tokens),
+                                     _stream(stream)))
+    return out
+
+
 def kv_cache_write(k_new: torch.Tensor, v_new: Optional[torch.Tensor], slots: torch.Tensor,
                    k_cache: torch.Tensor, v_cache: Optional[torch.Tensor], stream=None) -> None:
     """k_new [N, Hkv, Dk] bf16 -> k_cache [num_blocks, block_size, Hkv, Dk] (V likewise)."""

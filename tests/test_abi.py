@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     lib = psw.load()
-    assert lib.psw_abi_version() == 2
+    assert lib.psw_abi_version() == 3
     assert lib.psw_status_string(PSW_OK) == b"ok"
     assert lib.psw_status_string(PSW_ERR_INVALID) == b"invalid argument"
 

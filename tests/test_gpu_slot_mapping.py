@@ -121,3 +121,103 @@ def test_request_search_across_counts(R):
     got = _gpu_slots(qsl, pos, bt, B, M)
     ref = slot_mapping_ref(qsl, pos, bt, B, M)
     assert np.array_equal(got, ref)
+
+
+# ---- one context-parallel rank and the circular cache ----------------------
+
+from oracle import slot_mapping_cp_ref  # noqa: E402
+
+
+def _gpu_cp(qsl, pos, bt, B, M, kvb, world, rank, inter, circular=False):
+    return psw.slot_mapping_cp(i32(qsl), i64(pos), i32(bt), B, M, kv_cache_block_size=kvb,
+                               cp_world_size=world, cp_rank=rank, cp_interleave=inter,
+                               circular=circular).cpu().numpy()
+
+
+def test_cp_worked_example_from_the_page():
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "slot_mapping_cp_example.json")))
+    pos = np.arange(384, dtype=np.int64)
+    bt = np.array([[9, 2, 30, 1]], dtype=np.int32)
+    for rank in range(g["cp_world_size"]):
+        args = ([0, 384], pos, bt, g["block_size"], 400, g["kv_cache_block_size"],
+                g["cp_world_size"], rank, g["cp_interleave"])
+        assert np.array_equal(_gpu_cp(*args), slot_mapping_cp_ref(*args))
+
+
+# (world, interleave, block size, kv-cache block size): powers of two take the
+# shift path, the others the division path; world 1 is the plain mapping
+CP_GEOMS = [(2, 128, 128, 128), (8, 16, 16, 64), (4, 1, 16, 16), (8, 64, 16, 128),
+            (3, 16, 16, 64), (6, 4, 8, 24), (5, 3, 3, 9), (1, 4, 16, 64), (2, 8, 16, 32)]
+
+
+@pytest.mark.parametrize("geom", CP_GEOMS)
+def test_cp_random_batches_every_rank(geom):
+    world, inter, B, kvb = geom
+    rng = np.random.default_rng(sum(v * 31 ** i for i, v in enumerate(geom)))
+    R = int(rng.integers(1, 12))
+    stride = 40
+    bt = rng.integers(-1, 3000, size=(R, stride)).astype(np.int32)
+    qls = rng.integers(0, 200, size=R) * (rng.random(R) > 0.2)
+    qsl = np.concatenate([[0], np.cumsum(qls)]).astype(np.int32)
+    N = int(qsl[-1])
+    span = stride * kvb * world // max(1, kvb // B) + 5
+    pos = rng.integers(-3, span, size=N).astype(np.int64)
+    M = N + int(rng.integers(0, 70))
+    for rank in range(world):
+        got = _gpu_cp(qsl, pos, bt, B, M, kvb, world, rank, inter)
+        ref = slot_mapping_cp_ref(qsl, pos, bt, B, M, kvb, world, rank, inter)
+        assert np.array_equal(got, ref), (geom, rank)
+
+
+@pytest.mark.parametrize("B", [16, 12])
+def test_circular_cache(B):
+    rng = np.random.default_rng(B)
+    R = 9
+    bt = rng.integers(0, 500, size=(R, 3)).astype(np.int32)
+    qls = rng.integers(0, 50, size=R)
+    qsl = np.concatenate([[0], np.cumsum(qls)]).astype(np.int32)
+    N = int(qsl[-1])
+    pos = rng.integers(-5, 100000, size=N).astype(np.int64)
+    got = _gpu_cp(qsl, pos, bt, B, N + 11, B, 1, 0, 1, circular=True)
+    ref = slot_mapping_cp_ref(qsl, pos, bt, B, N + 11, B, 1, 0, 1, circular=True)
+    assert np.array_equal(got, ref)
+
+
+def test_cp_scaled_batch_sampled():
+    """A large batch (about 1.1 M tokens) on ranks 0 and 5 of 8; the oracle
+    checks a sample of requests, and over the 8 ranks every position of a
+    sampled request is mapped by exactly one."""
+    rng = np.random.default_rng(88)
+    R, B, kvb, world, inter = 512, 16, 64, 8, 16
+    lens = rng.integers(512, 4096, size=R)
+    need = -(-lens // (kvb * world)) * (kvb // B)   # logical blocks one rank needs
+    bt = np.full((R, int(need.max())), -1, dtype=np.int32)
+    perm = rng.permutation(int(need.sum())).astype(np.int32)
+    off = 0
+    for r in range(R):
+        bt[r, :need[r]] = perm[off:off + need[r]]
+        off += need[r]
+    qsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    pos = np.concatenate([np.arange(L) for L in lens]).astype(np.int64)
+    M = int(qsl[-1]) + 1000
+    outs = {rank: _gpu_cp(qsl, pos, bt, B, M, kvb, world, rank, inter) for rank in range(world)}
+    owners = np.stack([outs[r][:qsl[-1]] != -1 for r in range(world)]).sum(axis=0)
+    assert (owners == 1).all()
+    for rank in (0, 5):
+        for r in rng.choice(R, 12, replace=False):
+            sub = np.array([0, lens[r]], dtype=np.int32)
+            ref = slot_mapping_cp_ref(sub, pos[qsl[r]:qsl[r + 1]], bt[r:r + 1], B, int(lens[r]),
+                                      kvb, world, rank, inter)
+            assert np.array_equal(outs[rank][qsl[r]:qsl[r + 1]], ref)
+        assert (outs[rank][qsl[-1]:] == -1).all()
+
+
+def test_cp_invalid_geometry_is_rejected():
+    qsl, pos, bt = i32([0, 2]), i64([0, 1]), i32(np.zeros((1, 4)))
+    for kw in (dict(kv_cache_block_size=24), dict(cp_interleave=3), dict(cp_rank=2),
+               dict(cp_world_size=0), dict(circular=True)):
+        args = dict(kv_cache_block_size=32, cp_world_size=2, cp_rank=0, cp_interleave=8)
+        args.update(kw)
+        with pytest.raises(psw.PswError):
+            psw.slot_mapping_cp(qsl, pos, bt, 16, 2, **args)
