@@ -37,6 +37,7 @@
 //   * a wave skips tiles outside the union of its rows' allowed intervals, and
 //     masks per element only tiles not inside every row's interval (each row's
 //     allowed keys form one interval).
+#include <type_traits>
 #include <utility>
 
 #include "asm_ops.h"
@@ -251,7 +252,10 @@ prefill_attention_kernel(const AttnParams p) {
       int64_t lo;
       uint32_t voff;
       bool fast;
+      const char* kb;  // uniform K and V bases of this wave's first instruction
+      const char* vb;
     };
+    const int64_t wave_row = (int64_t)wave * S::kInstrPerWave * pitch;
     auto plan_tile = [&](int tile) __attribute__((always_inline)) {
       DmaPlan d;
       d.fast = false;
@@ -268,19 +272,28 @@ prefill_attention_kernel(const AttnParams p) {
       const int64_t seg1 = ((int64_t)b1 << bs_log2) * pitch;
       d.lo = two_segs ? min(seg0, seg1) : seg0;
       const int64_t delta = two_segs ? max(seg0, seg1) - d.lo : 0;
-      d.fast = first + S::kTile <= seq_len && delta < ((int64_t)1 << 31);
+      // every lane offset (segment distance + row within the tile + chunk +
+      // instruction row) must fit in 32 bits
+      d.fast = first + S::kTile <= seq_len &&
+               delta + (int64_t)(S::kTile + S::kInstrPerTile) * pitch + 1024 < ((int64_t)1 << 31);
       const bool lane_far = lane_second ? seg1 > seg0 : seg0 > seg1;
       d.voff = lane_off + (lane_far ? (uint32_t)delta : 0u);
+      d.kb = kbase + (d.lo + wave_row);
+      d.vb = vbase + (d.lo + wave_row);
       return d;
     };
     // instruction i of this wave (K, then V), fast path
+    // instruction i: uniform base + one 32-bit lane offset (the segment
+    // distance and i rows of the cache fit in 32 bits on the fast path)
+    const uint32_t pitch32 = (uint32_t)pitch;
     auto dma_k = [&](const DmaPlan& d, int buf, int i) __attribute__((always_inline)) {
       const int g = wave * S::kInstrPerWave + i;
-      lds_dma16(kbase + d.lo + g * pitch + d.voff, smem + buf * S::kBufBytes + g * S::kKBlock);
+      lds_dma16(d.kb + (uint32_t)(d.voff + (uint32_t)i * pitch32),
+                smem + buf * S::kBufBytes + g * S::kKBlock);
     };
     auto dma_v = [&](const DmaPlan& d, int buf, int i) __attribute__((always_inline)) {
       const int g = wave * S::kInstrPerWave + i;
-      lds_dma16(vbase + d.lo + g * pitch + d.voff,
+      lds_dma16(d.vb + (uint32_t)(d.voff + (uint32_t)i * pitch32),
                 smem + buf * S::kBufBytes + S::kKBytes + g * S::kVBlock);
     };
     auto issue_tile = [&](int tile, int buf, const DmaPlan& d) __attribute__((always_inline)) {
@@ -362,9 +375,12 @@ prefill_attention_kernel(const AttnParams p) {
       }
       const uint32_t kt = smem0 + (uint32_t)(buf * S::kBufBytes);
 
-      // S^T[key][row] for the 32 keys; K k-chunks read KA ahead
+      // S^T[key][row] for the 32 keys; K k-chunks read KA ahead.  Two copies
+      // of the sequence, with and without the DMA of tile tn, so that no
+      // branch sits between the MFMAs.
       f32x16 s;
-      {
+      auto score = [&](auto with_dma) __attribute__((always_inline)) {
+        constexpr bool DMA = decltype(with_dma)::value;
         constexpr int N = S::kQFrags, KA = 3;
         const uint32_t ka = kt + k_lane;
         bf16x8 kf[KA + 1];
@@ -380,13 +396,12 @@ prefill_attention_kernel(const AttnParams p) {
           s = mfma32(kf[c % (KA + 1)], qf[c], s);
           if constexpr (c + KA < N) kf[(c + KA) % (KA + 1)] = lds_read_b128_at<(c + KA) * 32>(ka);
           constexpr int step = N / S::kInstrPerWave;
-          if constexpr (c % step == 0) {
-            if (inter) dma_k(nd, bn, c / step);
-          } else if constexpr (c % step == step / 2) {
-            if (inter) dma_v(nd, bn, c / step);
-          }
+          if constexpr (DMA && c % step == 0) dma_k(nd, bn, c / step);
+          if constexpr (DMA && c % step == step / 2) dma_v(nd, bn, c / step);
         });
-      }
+      };
+      if (inter) score(std::true_type{});
+      else score(std::false_type{});
       if (!(base >= wave_lo && base + S::kTile - 1 <= wave_hi)) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
