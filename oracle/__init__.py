@@ -23,3 +23,4 @@ from .tile_bounds import tile_bounds_ref  # noqa: F401
 from .attention import attention_ref, attention_pruned_ref  # noqa: F401
 from .lse_merge import lse_merge_ref  # noqa: F401
 from .kv_cache import kv_cache_write_ref  # noqa: F401
+from .vup import vup_projection_ref  # noqa: F401
