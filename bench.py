@@ -353,8 +353,14 @@ def bench_decode(args, torch, psw, np):
                                  out_dtype=0, num_splits=P)
     ws = torch.empty(max(1, psw.ops.attention_workspace_size(ws_args)), dtype=torch.uint8,
                      device="cuda")
+    # V-up projection of the merged output (128 heads x 512 -> 128 per head)
+    dv_up = 128
+    from workloads.synth import f32_to_bf16_bits
+    w_uv = bits_to_bf16(f32_to_bf16_bits(
+        np.random.default_rng(55).standard_normal((H, DV, dv_up)).astype(np.float32) / DV ** 0.5))
+    vup_out = torch.empty((R, H * dv_up), dtype=torch.bfloat16, device="cuda")
     steps = max(args.steps, 10)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
 
     def step(i=None):
         psw.slot_mapping(qsl, positions, bt, B, R, out=slots)
@@ -369,6 +375,9 @@ def bench_decode(args, torch, psw, np):
         psw.lse_combine(outs, lses, out=out)
         if i is not None:
             ev[i][2].record()
+        psw.vup_projection(out, w_uv, out=vup_out)
+        if i is not None:
+            ev[i][3].record()
 
     log("timing decode")
     for _ in range(args.warmup):
@@ -384,8 +393,13 @@ def bench_decode(args, torch, psw, np):
     ms = t0.elapsed_time(t1) / steps
     attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     comb_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    vup_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
+    vup_bytes = out.numel() * 2 + w_uv.numel() * 2 + vup_out.numel() * 2
     kv_bytes = int(w.seq_lens.sum()) * w.head_dim_qk * 2
-    alg_bytes = (kv_bytes + q.numel() * 2 + w.block_table.size * 4 + out.numel() * 2)
+    # KV rows once + Q + block table + W_UV + the projected output (the merged
+    # latent output is an intermediate)
+    alg_bytes = (kv_bytes + q.numel() * 2 + w.block_table.size * 4 + w_uv.numel() * 2
+                 + vup_out.numel() * 2)
     gbs = alg_bytes / (ms * 1e-3) / 1e9
     attn_gbs = (kv_bytes + q.numel() * 2) / (attn_ms * 1e-3) / 1e9
     return {
@@ -398,11 +412,14 @@ def bench_decode(args, torch, psw, np):
         "attention_ms": round(attn_ms, 5),
         "attention_GBps": round(attn_gbs, 1),
         "combine_ms": round(comb_ms, 5),
+        "vup_projection": {"ms": round(vup_ms, 5), "algorithmic_bytes": vup_bytes,
+                           "GBps": round(vup_bytes / (vup_ms * 1e-3) / 1e9, 1),
+                           "shape": f"[{R}, {H}, {DV}] x [{H}, {DV}, {dv_up}]"},
         "history_splits": S,
         "partials": P,
         "partial_dtype": args.decode_partials,
         "step": "slot_mapping + kv_cache_write + history and current partials (one call) "
-                "+ lse_combine",
+                "+ lse_combine + vup_projection",
     }
 
 

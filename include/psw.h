@@ -131,6 +131,24 @@ int psw_kv_cache_write(const void* k_new, const void* v_new, const int32_t* slot
                        void* stream);
 
 /*
+ * psw_vup_projection - MLA DCP decode notes (vllm-ascend PR #16977), "Terms"
+ * (the latent attention output is projected back to each head's V dimension),
+ * section 1.1 (the merged output is batch-major) and code block A (one
+ * batched product per head, no transposes):
+ *     out[t, h, :] = x[t, h, :] @ w_uv[h]          fp32 accumulation, bf16 result
+ *   x     bf16 [num_tokens, num_heads, kv_lora_rank], contiguous (device) - e.g. the
+ *         psw_lse_combine output viewed as [tokens, heads, rank]
+ *   w_uv  bf16 [num_heads, kv_lora_rank, v_head_dim], contiguous (device)
+ *   out   bf16 [num_tokens, num_heads, v_head_dim], contiguous (device), caller-owned
+ * Errors: PSW_ERR_INVALID for negative sizes or a NULL pointer with work to do;
+ * PSW_ERR_UNSUPPORTED unless kv_lora_rank is 128, 256 or 512 and v_head_dim is a
+ * positive multiple of 64.
+ */
+int psw_vup_projection(const void* x, const void* w_uv, void* out, int32_t num_tokens,
+                       int32_t num_heads, int32_t kv_lora_rank, int32_t v_head_dim,
+                       void* stream);
+
+/*
  * Arguments of psw_swa_mm_attention and psw_tile_bounds.
  *
  * Mask ([SWA-MM] "Implementation breakdown" items 1-2, "Key source snippet",

@@ -12,5 +12,6 @@ from .ops import (  # noqa: F401
     slot_mapping_cp,
     swa_mm_attention,
     tile_bounds,
+    vup_projection,
 )
 from ._lib import LIB_PATH, PswError, load  # noqa: F401

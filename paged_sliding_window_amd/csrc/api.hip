@@ -284,6 +284,24 @@ int psw_lse_combine(const void* const* partial_out, const float* const* partial_
                    "lse_combine");
 }
 
+int psw_vup_projection(const void* x, const void* w_uv, void* out, int32_t num_tokens,
+                       int32_t num_heads, int32_t kv_lora_rank, int32_t v_head_dim,
+                       void* stream) {
+  if (num_tokens < 0 || num_heads < 0 || kv_lora_rank < 1 || v_head_dim < 1)
+    return fail(PSW_ERR_INVALID, "num_tokens %d, num_heads %d, kv_lora_rank %d, v_head_dim %d",
+                num_tokens, num_heads, kv_lora_rank, v_head_dim);
+  if (!psw::vup_supported(kv_lora_rank, v_head_dim))
+    return fail(PSW_ERR_UNSUPPORTED, "kv_lora_rank %d / v_head_dim %d (need 128, 256 or 512 / a "
+                "multiple of 64)", kv_lora_rank, v_head_dim);
+  if (num_tokens > 0 && num_heads > 0 && (x == nullptr || w_uv == nullptr || out == nullptr))
+    return fail(PSW_ERR_INVALID, "x, w_uv and out are required");
+  return check_hip(psw::launch_vup_projection(static_cast<const uint16_t*>(x),
+                                              static_cast<const uint16_t*>(w_uv),
+                                              static_cast<uint16_t*>(out), num_tokens, num_heads,
+                                              kv_lora_rank, v_head_dim, (hipStream_t)stream),
+                   "vup_projection");
+}
+
 int psw_tile_bounds(const psw_attn_args* geometry, int32_t tile_size, int32_t block_m,
                     int32_t block_q, const int32_t* seq_idx, const int32_t* q_block_idx,
                     int32_t num_queries, int32_t* out, void* stream) {

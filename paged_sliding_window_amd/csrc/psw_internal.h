@@ -53,6 +53,12 @@ hipError_t launch_lse_combine(const CombineArgs& parts, int num_partials, int pa
                               int64_t num_rows, int head_dim_v, void* out, int out_f32,
                               float* out_lse, hipStream_t stream);
 
+// V-up projection: out[t, h, :] = x[t, h, :] @ w[h] (bf16 in and out, fp32 accumulation).
+bool vup_supported(int kv_lora_rank, int v_head_dim);
+hipError_t launch_vup_projection(const uint16_t* x, const uint16_t* w, uint16_t* out,
+                                 int num_tokens, int num_heads, int kv_lora_rank, int v_head_dim,
+                                 hipStream_t stream);
+
 hipError_t launch_tile_bounds(const int32_t* qsl, const int32_t* seq_lens,
                               const int32_t* mm_ranges, int max_mm_ranges, int queries_per_kv,
                               MaskGeom geom, int tile, int block_m, int block_q,

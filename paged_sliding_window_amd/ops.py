@@ -217,6 +217,28 @@ def lse_combine(partial_outs: Sequence[torch.Tensor], partial_lses: Sequence[tor
     return out if out_lse is None else (out, out_lse)
 
 
+def vup_projection(x: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """x bf16 [T, H, R] (or [T * H, R]) @ w_uv bf16 [H, R, Dv] per head -> [T, H, Dv]."""
+    _need(w_uv, "w_uv", torch.bfloat16, 3)
+    H, R, Dv = w_uv.shape
+    _need(x, "x", torch.bfloat16)
+    if x.dim() == 2:
+        if x.shape[0] % H != 0:
+            raise ValueError("x rows must be a multiple of the head count")
+        x = x.view(x.shape[0] // H, H, x.shape[1])
+    if x.dim() != 3 or x.shape[1] != H or x.shape[2] != R:
+        raise ValueError(f"x {tuple(x.shape)} does not match w_uv {tuple(w_uv.shape)}")
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, H, Dv), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != T * H * Dv:
+        raise ValueError("out must hold num_tokens * num_heads * v_head_dim elements")
+    check(load().psw_vup_projection(_ptr(x), _ptr(w_uv), _ptr(out), T, H, R, Dv, _stream(stream)))
+    return out
+
+
 def tile_bounds(query_start_loc: torch.Tensor, seq_lens: torch.Tensor,
                 mm_ranges: Optional[torch.Tensor], *, num_q_heads: int, num_kv_heads: int,
                 window: int, causal: bool, chunk_size: int, chunk_lookback: int, tile_size: int,
