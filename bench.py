@@ -229,6 +229,8 @@ def main():
         log("decode half")
         result["decode"] = bench_decode(args, torch, psw, np)
 
+    log("segmented splits, non-causal workload")
+    result["prefill_segmented"] = bench_segmented(torch, psw)
     log("slot mapping, scaled batch")
     result["slot_mapping_scaled"] = bench_slot_mapping(torch, psw, np)
     if not args.skip_cpu:
@@ -236,6 +238,51 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w)
     result["setup_s"] = round(time.perf_counter() - t_setup, 1)
     print(json.dumps(result), flush=True)
+
+
+def bench_segmented(torch, psw, splits=4, reps=20):
+    """The non-causal chunk-lookback workload (2 x 4,096 tokens, 8 heads, d 128):
+    with 128-row query blocks it has 528 workgroups, one round of the GPU's
+    512 slots plus a few; segmented splits (each block's tile loop cut into
+    `splits` pieces, merged by the LSE combine) spread the same tiles over
+    more, shorter workgroups.  Reports both times; not part of the step."""
+    from tests.gpu_setup import GpuWorkload
+    from workloads import make_config
+    w = make_config(4)
+    gw = GpuWorkload(w)
+    N, Hq, D = w.num_tokens, w.num_q_heads, w.head_dim_v
+    kw = dict(scale=w.scale, window=w.window, causal=w.causal, chunk_size=w.chunk_size,
+              chunk_lookback=w.chunk_lookback, mm_ranges=gw.mm_ranges)
+    out = torch.empty((N, Hq, D), dtype=torch.bfloat16, device="cuda")
+    parts = torch.empty((splits, N, Hq, D), dtype=torch.bfloat16, device="cuda")
+    lses = torch.empty((splits, N, Hq), dtype=torch.float32, device="cuda")
+    pl = [parts[j].view(N * Hq, D) for j in range(splits)]
+    ll = [lses[j].view(N * Hq) for j in range(splits)]
+
+    def unsplit():
+        psw.swa_mm_attention(gw.q, gw.k_cache, gw.v_cache, gw.block_table, gw.qsl, gw.seq_lens,
+                             out=out, **kw)
+
+    def segmented():
+        psw.swa_mm_attention(gw.q, gw.k_cache, gw.v_cache, gw.block_table, gw.qsl, gw.seq_lens,
+                             out=parts, lse=lses, num_splits=splits, **kw)
+        psw.lse_combine(pl, ll, out=out.view(N * Hq, D))
+
+    res = {"workload": "noncausal_chunk_lookback_2x4096", "splits": splits}
+    for name, fn in (("unsplit_ms", unsplit), ("segmented_with_combine_ms", segmented)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) / reps, 5)
+    del gw
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_slot_mapping(torch, psw, np, num_reqs=4096, seed=7):

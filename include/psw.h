@@ -180,7 +180,8 @@ typedef struct psw_attn_args {
   const int32_t* query_start_loc; /* int32 [num_seqs + 1] */
   const int32_t* seq_lens;        /* int32 [num_seqs], total keys incl. cached context */
   const int32_t* mm_ranges;       /* int32 [num_seqs, max_mm_ranges, 2] or NULL (no images) */
-  const int32_t* key_ranges;      /* int32 [num_splits, num_seqs, 2] or NULL (one split) */
+  const int32_t* key_ranges;      /* int32 [num_splits, num_seqs, 2], or NULL: one split, or
+                                     segmented splits when num_splits > 1 (see below) */
   void* out;                      /* out_dtype [num_splits, num_tokens, num_q_heads, head_dim_v] */
   float* lse;                     /* fp32 [num_splits, num_tokens, num_q_heads] or NULL */
   int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v;
@@ -188,7 +189,7 @@ typedef struct psw_attn_args {
   int32_t window;                 /* > 0: sliding window; <= 0: none */
   int32_t causal;                 /* 1: causal base; 0: bidirectional base */
   int32_t chunk_size, chunk_lookback;  /* chunk_lookback < 0: off */
-  int32_t num_splits;             /* >= 1; must be 1 when key_ranges == NULL */
+  int32_t num_splits;             /* >= 1 */
   int32_t out_dtype;              /* PSW_BF16 or PSW_F32 */
   float scale;                    /* softmax scale */
   void* workspace;                /* device scratch of >= psw_attention_workspace_size() bytes,
@@ -206,12 +207,24 @@ typedef struct psw_attn_args {
  * 1 <= query_len <= seq_len for every request with new tokens; block-table
  * entries for every key below seq_len are valid blocks of the caches; image
  * ranges lie in [0, seq_len).
+ * Splits.  With key_ranges, split s covers keys [key_ranges[s][r][0],
+ * key_ranges[s][r][1]) of request r.  Without key_ranges and num_splits > 1
+ * (segmented splits, [SWA-MM] "Key source snippet": the tile loop of a query
+ * block is the unit of work), each query block's tile interval [lo, hi) is cut
+ * into num_splits pieces of ceil((hi - lo) / num_splits) tiles, split s taking
+ * the s-th (possibly empty); query blocks are 128 rows (128 / (num_q_heads /
+ * num_kv_heads) positions of one request) and tiles 32 keys.  Either way each
+ * split writes its partial output and LSE (-inf and a zero row where the split
+ * sees no allowed key), and psw_lse_combine over the splits gives the unsplit
+ * result.  Segmented splits serve the prefill shapes, whose work is one
+ * workgroup per (query block, KV head, split); the latent decode balances its
+ * own work and takes splits only as key ranges.
  * Errors: PSW_ERR_INVALID (struct_size mismatch, counts < 0, num_q_heads not a
  * multiple of num_kv_heads, block_size not a power of two, chunk_size < 1 with
- * chunk_lookback >= 0, num_splits < 1, num_splits > 1 without key_ranges, NULL
- * pointer, workspace missing, misaligned or smaller than
- * psw_attention_workspace_size()), PSW_ERR_UNSUPPORTED (head dims / dtype
- * combination without a kernel).
+ * chunk_lookback >= 0, num_splits < 1, NULL pointer, workspace missing,
+ * misaligned or smaller than psw_attention_workspace_size()),
+ * PSW_ERR_UNSUPPORTED (head dims / dtype combination without a kernel;
+ * segmented splits with the latent decode shape).
  */
 int psw_swa_mm_attention(const psw_attn_args* args, void* stream);
 

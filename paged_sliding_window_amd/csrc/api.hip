@@ -176,8 +176,8 @@ static int fill_geometry(const psw_attn_args* a, psw::AttnParams& p, bool need_t
       return fail(PSW_ERR_INVALID, "block_size %d must be a power of two", a->block_size);
     if (a->block_table_stride < 1)
       return fail(PSW_ERR_INVALID, "block_table_stride %d must be >= 1", a->block_table_stride);
-    if (a->num_splits < 1 || (a->num_splits > 1 && a->key_ranges == nullptr))
-      return fail(PSW_ERR_INVALID, "num_splits %d needs key_ranges when > 1", a->num_splits);
+    if (a->num_splits < 1)
+      return fail(PSW_ERR_INVALID, "num_splits %d must be >= 1", a->num_splits);
     if (a->out_dtype != PSW_BF16 && a->out_dtype != PSW_F32)
       return fail(PSW_ERR_INVALID, "out_dtype %d unknown", a->out_dtype);
     if (!(a->scale > 0.f) || !std::isfinite(a->scale))
@@ -238,6 +238,10 @@ int psw_swa_mm_attention(const psw_attn_args* args, void* stream) {
   int st = fill_geometry(args, p, true);
   if (st != PSW_OK) return st;
   const bool latent = args->v_cache == nullptr;
+  if (latent && args->key_ranges == nullptr && args->num_splits > 1)
+    return fail(PSW_ERR_UNSUPPORTED, "segmented splits (num_splits %d without key_ranges) are "
+                "for the prefill shapes; the latent decode balances its own work",
+                args->num_splits);
   if (p.num_tokens == 0 || p.num_seqs == 0) return ok();
   const int64_t need = workspace_needed(args, p);
   if (need > 0 && (args->workspace == nullptr || args->workspace_bytes < need ||

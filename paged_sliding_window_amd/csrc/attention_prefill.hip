@@ -141,8 +141,17 @@ prefill_attention_kernel(const AttnParams p) {
   const RangesWave rg{ranges, p.max_mm_ranges};  // every lane is active here
   const TileRange tr = tile_bounds_r(ctx, seq_len, query_len, q_block, S::kTile, block_q * qpk,
                                      block_q, qpk, p.geom, rg);
-  const int t_lo = max(tr.lo, key_begin / S::kTile);
-  const int t_hi = min(tr.hi, (key_end + S::kTile - 1) / S::kTile);
+  int t_lo = max(tr.lo, key_begin / S::kTile);
+  int t_hi = min(tr.hi, (key_end + S::kTile - 1) / S::kTile);
+  if (p.key_ranges == nullptr && p.num_splits > 1) {
+    // segmented split: split s takes tiles [lo + s * seg, lo + (s + 1) * seg) of
+    // the block's interval, seg = ceil(tiles / splits)
+    const int n = max(0, t_hi - t_lo);
+    const int seg = (n + p.num_splits - 1) / p.num_splits;
+    const int s_lo = min(t_lo + split * seg, t_hi);
+    t_hi = min(t_hi, s_lo + seg);
+    t_lo = s_lo;
+  }
 
   // ---- this lane's query row ----------------------------------------------
   const int r = wave * S::kRowsPerWave + (lane & 31);

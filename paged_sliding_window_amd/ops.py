@@ -128,10 +128,13 @@ def swa_mm_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[t
                      key_ranges: Optional[torch.Tensor] = None, head_dim_v: Optional[int] = None,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                      out_dtype: torch.dtype = torch.bfloat16, return_lse: bool = False,
+                     num_splits: Optional[int] = None,
                      workspace: Optional[torch.Tensor] = None, stream=None):
     """Paged attention; with key_ranges [S, num_seqs, 2] it writes S fp32/bf16
-    partials out[S, N, Hq, Dv] and lse[S, N, Hq].  ``workspace`` (uint8, device)
-    is allocated here when the call needs one and none is given."""
+    partials out[S, N, Hq, Dv] and lse[S, N, Hq]; without key_ranges,
+    num_splits = S > 1 asks for S segmented splits of every query block's tile
+    loop (partials of the same shape).  ``workspace`` (uint8, device) is
+    allocated here when the call needs one and none is given."""
     _need(q, "q", torch.bfloat16, 3)
     _need(k_cache, "k_cache", torch.bfloat16, 4)
     if v_cache is not None:
@@ -144,10 +147,13 @@ def swa_mm_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[t
     _need(seq_lens, "seq_lens", torch.int32, 1)
     if mm_ranges is not None:
         _need(mm_ranges, "mm_ranges", torch.int32, 3)
-    num_splits = 1
     if key_ranges is not None:
         _need(key_ranges, "key_ranges", torch.int32, 3)
+        if num_splits is not None and num_splits != key_ranges.shape[0]:
+            raise ValueError("num_splits differs from the number of key ranges")
         num_splits = key_ranges.shape[0]
+    elif num_splits is None:
+        num_splits = 1
     n, hq = q.shape[0], q.shape[1]
     odt = {torch.bfloat16: PSW_BF16, torch.float32: PSW_F32}[out_dtype]
     if out is None:
@@ -173,7 +179,7 @@ def swa_mm_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[t
         _need(workspace, "workspace", torch.uint8)
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
     check(load().psw_swa_mm_attention(ctypes.byref(a), _stream(stream)))
-    if key_ranges is None:
+    if key_ranges is None and num_splits == 1:
         out = out.view(n, hq, head_dim_v)
         if lse is not None:
             lse = lse.view(n, hq)

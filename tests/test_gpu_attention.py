@@ -113,3 +113,59 @@ def test_empty_batch_is_a_no_op():
                                scale=1.0, window=0, causal=True)
     torch.cuda.synchronize()
     assert out.numel() == 0
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_segmented_splits_partials_and_combine(seed):
+    """Segmented splits: each query block's tile loop cut into S pieces.  Every
+    piece must equal the oracle over exactly its keys (the block's tile
+    interval from the oracle's tile bounds at the kernel's tiling: 128-row
+    blocks, 32-key tiles), and the LSE combine of the S pieces the unsplit
+    attention."""
+    import paged_sliding_window_amd as psw
+    from oracle import tile_bounds_ref
+    rng = np.random.default_rng(900 + seed)
+    d = int(rng.choice([64, 128, 256]))
+    hkv = int(rng.choice([1, 2]))
+    qpk = int(rng.choice([1, 2, 8]))
+    w = make_small_case(900 + seed, num_seqs=int(rng.integers(1, 4)), max_len=700, hq=hkv * qpk,
+                        hkv=hkv, d=d, block_size=16)
+    gw = GpuWorkload(w)
+    S = int(rng.choice([2, 3, 5]))
+    parts, lses = gw.attention(num_splits=S, out_dtype=torch.float32)
+    N, Hq = w.num_tokens, w.num_q_heads
+    merged, merged_lse = psw.lse_combine([parts[j].reshape(N * Hq, d) for j in range(S)],
+                                         [lses[j].reshape(N * Hq) for j in range(S)],
+                                         out_dtype=torch.float32, out_lse=torch.empty(
+                                             N * Hq, dtype=torch.float32, device="cuda"))
+    parts, lses = parts.cpu().numpy(), lses.cpu().numpy()
+    merged = merged.cpu().numpy().reshape(N, Hq, d)
+    merged_lse = merged_lse.cpu().numpy().reshape(N, Hq)
+    block_q, T = 128 // qpk, 32
+    use_mm = w.max_mm_ranges > 0 and (w.mm_ranges != 0).any()
+    for r in range(w.num_seqs):
+        s0, ql = int(w.query_start_loc[r]), int(w.query_lens[r])
+        ref_o, ref_l = oracle_rows(w, r)
+        assert_close(merged[s0:s0 + ql], ref_o, f"seq {r} combined")
+        assert_lse_close(merged_lse[s0:s0 + ql], ref_l, f"seq {r} combined lse")
+        for qb in range(-(-ql // block_q)):
+            lo, hi, _ = tile_bounds_ref(int(w.context_lens[r]), int(w.seq_lens[r]), ql, qb, T,
+                                        block_q * qpk, block_q, qpk, w.window, use_mm, w.causal,
+                                        w.chunk_lookback, w.chunk_size, w.ranges_of(r))
+            seg = -(-(hi - lo) // S) if hi > lo else 0
+            rows = np.arange(qb * block_q, min(ql, (qb + 1) * block_q))
+            for j in range(S):
+                a = min(lo + j * seg, hi)
+                b = min(hi, a + seg)
+                o_j, l_j = oracle_rows(w, r, rows=rows, key_range=(a * T, b * T))
+                assert_close(parts[j, s0 + rows], o_j, f"seq {r} block {qb} piece {j}")
+                assert_lse_close(lses[j, s0 + rows], l_j, f"seq {r} block {qb} piece {j} lse")
+
+
+def test_segmented_splits_rejected_for_the_latent_decode():
+    import paged_sliding_window_amd as psw
+    w = make_small_case(4, num_seqs=2, max_len=200, hq=32, hkv=1, d=576, dv=512, window=0,
+                        causal=True, chunk=(0, -1), max_ranges=0, latent=True, block_size=64)
+    gw = GpuWorkload(w)
+    with pytest.raises(psw.PswError):
+        gw.attention(num_splits=2, out_dtype=torch.float32)
