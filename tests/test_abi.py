@@ -8,7 +8,8 @@ import re
 import pytest
 
 import paged_sliding_window_amd as psw
-from paged_sliding_window_amd._lib import (EXPORTS, PSW_ERR_INVALID, PSW_OK, PswAttnArgs)
+from paged_sliding_window_amd._lib import (EXPORTS, PSW_ERR_INVALID, PSW_ERR_UNSUPPORTED, PSW_OK,
+                                            PswAttnArgs)
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "psw.h")
 
@@ -57,7 +58,7 @@ def test_struct_size_matches_the_c_struct():
 
 
 @pytest.mark.parametrize("field,value", [
-    ("num_q_heads", 7), ("block_size", 12), ("scale", 0.0), ("num_splits", 2),
+    ("num_q_heads", 7), ("block_size", 12), ("scale", 0.0), ("num_splits", 0),
     ("out_dtype", 9), ("num_tokens", -1), ("chunk_size", 0),
 ])
 def test_attention_rejects_bad_scalars(field, value):
@@ -66,6 +67,12 @@ def test_attention_rejects_bad_scalars(field, value):
         kw["chunk_lookback"] = 1
     lib = psw.load()
     assert lib.psw_swa_mm_attention(ctypes.byref(_args(**kw)), None) == PSW_ERR_INVALID
+
+
+def test_segmented_splits_need_a_prefill_shape():
+    # v_cache NULL is the latent decode, which takes splits only as key ranges
+    lib = psw.load()
+    assert lib.psw_swa_mm_attention(ctypes.byref(_args(num_splits=2)), None) == PSW_ERR_UNSUPPORTED
 
 
 def test_other_entry_points_reject_bad_scalars():
