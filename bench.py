@@ -449,7 +449,17 @@ def bench_decode(args, torch, psw, np):
                  + vup_out.numel() * 2)
     gbs = alg_bytes / (ms * 1e-3) / 1e9
     attn_gbs = (kv_bytes + q.numel() * 2) / (attn_ms * 1e-3) / 1e9
+    def one_call():
+        psw.swa_mm_attention(q, cache, None, bt, qsl, seq_lens, scale=w.scale, window=0,
+                             causal=True, key_ranges=kr_all, head_dim_v=DV, out=part_o,
+                             lse=part_l, out_dtype=pdt, workspace=ws)
+        psw.lse_combine(outs, lses, out=out)
+
+    log("timing decode on two streams")
+    two = bench_two_streams(torch, psw, np, w, q, cache, bt, qsl, seq_lens, kr_all, S, pdt, out,
+                            one_call)
     return {
+        "two_streams": two,
         "workload": "mla_splitkv_decode_b64",
         "unit": "GB/s",
         "value": round(gbs, 1),
@@ -468,6 +478,61 @@ def bench_decode(args, torch, psw, np):
         "step": "slot_mapping + kv_cache_write + history and current partials (one call) "
                 "+ lse_combine + vup_projection",
     }
+
+
+def bench_two_streams(torch, psw, np, w, q, cache, bt, qsl, seq_lens, kr_all, S, pdt, out,
+                      one_call, reps=20, rounds=5):
+    """Attention + combine of the decode step four ways: the history splits and
+    the current key as ranges of one call; history then current as two calls on
+    one stream; history on the main stream and current on a side stream with
+    separate workspaces (they may overlap) or one shared workspace (current
+    after history), joined before the combine."""
+    DV = w.head_dim_v
+    hist, cur = kr_all[:S].contiguous(), kr_all[S:].contiguous()
+    side = torch.cuda.Stream()
+    kw = dict(scale=w.scale, window=0, causal=True, head_dim_v=DV)
+
+    def two_calls():
+        ho, hl = psw.swa_mm_attention(q, cache, None, bt, qsl, seq_lens, key_ranges=hist,
+                                      out_dtype=pdt, return_lse=True, **kw)
+        co, cl = psw.swa_mm_attention(q, cache, None, bt, qsl, seq_lens, key_ranges=cur,
+                                      out_dtype=pdt, return_lse=True, **kw)
+        rows = q.shape[0] * q.shape[1]
+        psw.lse_combine([ho[j].view(rows, DV) for j in range(S)] + [co[0].view(rows, DV)],
+                        [hl[j].view(rows) for j in range(S)] + [cl[0].view(rows)], out=out)
+
+    def streams(shared):
+        return lambda: psw.decode_two_streams(q, cache, None, bt, qsl, seq_lens,
+                                              history_ranges=hist, current_ranges=cur,
+                                              side_stream=side, partial_dtype=pdt,
+                                              shared_workspace=shared, out=out, **kw)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    # round-robin rounds, median per variant: the first timings of a run are
+    # slower while the clocks settle, which would favour whatever runs last
+    variants = {"one_call_ms": one_call, "two_calls_one_stream_ms": two_calls,
+                "two_streams_separate_workspaces_ms": streams(False),
+                "two_streams_shared_workspace_ms": streams(True)}
+    times = {k: [] for k in variants}
+    for _ in range(rounds):
+        for k, fn in variants.items():
+            times[k].append(timed(fn))
+    res = {k: round(float(np.median(v)), 5) for k, v in times.items()}
+    res["what"] = (f"attention + lse_combine of the decode step, median of {rounds} "
+                   f"round-robin rounds of {reps} calls")
+    return res
 
 
 if __name__ == "__main__":

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define PSW_ABI_VERSION 3
+#define PSW_ABI_VERSION 4
 
 enum psw_status {
   PSW_OK = 0,
@@ -256,6 +256,40 @@ int psw_lse_combine(const void* const* partial_out, const float* const* partial_
                     int32_t num_partials, int32_t partial_dtype, int64_t num_rows,
                     int32_t head_dim_v, void* out, int32_t out_dtype, float* out_lse,
                     void* stream);
+
+/*
+ * psw_decode_two_streams - [DCP] section 2.1 (the stream swap), section 3.2 and
+ * code blocks C and D: the history and current partials of a decode step on
+ * two streams, joined before their LSE combine on the main stream.
+ *   history   attention call over the history key ranges (num_splits partials),
+ *             enqueued on main_stream
+ *   current   attention call over the current key (its own partials), enqueued
+ *             on side_stream
+ *   out, out_dtype, out_lse  as psw_lse_combine, with num_rows = num_tokens x
+ *             num_q_heads and head_dim_v of the two calls
+ * Both calls are checked exactly as psw_swa_mm_attention checks one; they must
+ * agree in num_tokens, num_q_heads, head_dim_v and out_dtype (the partial
+ * dtype), both must write lse, and together hold at most 64 partials.  The
+ * combine reads history's partials 0 .. S_h - 1 and then current's, in place.
+ * Ordering: the side stream waits for an event recorded on main_stream, either
+ * before the history call (the two workspaces are disjoint: the current call
+ * sees everything enqueued on main_stream before this call and can run beside
+ * the history call) or after it (the workspaces overlap: the current call runs
+ * after the history call has finished with the shared workspace, as the pages
+ * order it).  main_stream then waits for an event recorded on side_stream after
+ * the current call, and runs the combine.  With main_stream == side_stream the
+ * three steps run in order on that stream.  The exchange of history partials
+ * between ranks, which the pages place on the main stream between the history
+ * call and the join, has no counterpart on one GPU.
+ * Tensors read or written on side_stream must stay alive until side_stream has
+ * passed them.  On its first call on a device this function creates two HIP
+ * events for that device (kept until the process ends); calls from several
+ * threads enqueue one at a time.  Errors: as psw_swa_mm_attention and
+ * psw_lse_combine; nothing is enqueued when a check fails.
+ */
+int psw_decode_two_streams(const psw_attn_args* history, const psw_attn_args* current,
+                           void* out, int32_t out_dtype, float* out_lse, void* main_stream,
+                           void* side_stream);
 
 /*
  * psw_tile_bounds - the per-query-block tile interval the attention kernel uses,

@@ -55,6 +55,8 @@ EXPORTS = {
     "psw_attention_workspace_size": (_i32, [ctypes.POINTER(PswAttnArgs), ctypes.POINTER(_i64)]),
     "psw_lse_combine": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _i32, _i64, _i32,
                                _vp, _i32, _vp, _vp]),
+    "psw_decode_two_streams": (_i32, [ctypes.POINTER(PswAttnArgs), ctypes.POINTER(PswAttnArgs), _vp,
+                                      _i32, _vp, _vp, _vp]),
     "psw_vup_projection": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "psw_tile_bounds": (_i32, [ctypes.POINTER(PswAttnArgs), _i32, _i32, _i32, _vp, _vp, _i32,
                                _vp, _vp]),

@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstring>
 #include <cstdarg>
+#include <mutex>
 
 #include "psw.h"
 #include "device_common.h"
@@ -233,30 +234,59 @@ int psw_attention_workspace_size(const psw_attn_args* args, int64_t* bytes) {
   return ok();
 }
 
-int psw_swa_mm_attention(const psw_attn_args* args, void* stream) {
-  psw::AttnParams p{};
+}  // extern "C"
+
+namespace {
+
+// Host checks of one attention call; on PSW_OK, p holds its parameters, latent
+// says which kernel family runs it and empty that there is nothing to launch.
+int prepare_attention(const psw_attn_args* args, psw::AttnParams& p, bool& latent, bool& empty,
+                      int64_t& workspace_used) {
   int st = fill_geometry(args, p, true);
   if (st != PSW_OK) return st;
-  const bool latent = args->v_cache == nullptr;
+  latent = args->v_cache == nullptr;
+  empty = p.num_tokens == 0 || p.num_seqs == 0;
+  workspace_used = 0;
   if (latent && args->key_ranges == nullptr && args->num_splits > 1)
     return fail(PSW_ERR_UNSUPPORTED, "segmented splits (num_splits %d without key_ranges) are "
                 "for the prefill shapes; the latent decode balances its own work",
                 args->num_splits);
-  if (p.num_tokens == 0 || p.num_seqs == 0) return ok();
+  if (empty) return PSW_OK;
   const int64_t need = workspace_needed(args, p);
   if (need > 0 && (args->workspace == nullptr || args->workspace_bytes < need ||
                    (reinterpret_cast<uintptr_t>(args->workspace) & 255) != 0))
     return fail(PSW_ERR_INVALID,
                 "workspace of %lld bytes (256-byte aligned) required, got %lld at %p",
                 (long long)need, (long long)args->workspace_bytes, args->workspace);
-  if (latent && psw::decode_supported(p))
-    return check_hip(psw::launch_attention_decode(p, args->workspace, (hipStream_t)stream),
-                     "attention(decode)");
-  if (psw::prefill_supported(p.head_dim_qk, p.head_dim_v, p.queries_per_kv, latent))
-    return check_hip(psw::launch_attention_prefill(p, (hipStream_t)stream), "attention(prefill)");
+  workspace_used = need;
+  if (latent && psw::decode_supported(p)) return PSW_OK;
+  if (psw::prefill_supported(p.head_dim_qk, p.head_dim_v, p.queries_per_kv, latent)) return PSW_OK;
   return fail(PSW_ERR_UNSUPPORTED,
               "no kernel for head dims %d/%d, %d query heads per KV head, %s V",
               p.head_dim_qk, p.head_dim_v, p.queries_per_kv, latent ? "latent" : "separate");
+}
+
+// Enqueues a call that prepare_attention accepted.
+int launch_prepared(const psw_attn_args* args, const psw::AttnParams& p, bool latent,
+                    hipStream_t stream) {
+  if (latent && psw::decode_supported(p))
+    return check_hip(psw::launch_attention_decode(p, args->workspace, stream),
+                     "attention(decode)");
+  return check_hip(psw::launch_attention_prefill(p, stream), "attention(prefill)");
+}
+
+}  // namespace
+
+extern "C" {
+
+int psw_swa_mm_attention(const psw_attn_args* args, void* stream) {
+  psw::AttnParams p{};
+  bool latent = false, empty = false;
+  int64_t ws = 0;
+  int st = prepare_attention(args, p, latent, empty, ws);
+  if (st != PSW_OK) return st;
+  if (empty) return ok();
+  return launch_prepared(args, p, latent, (hipStream_t)stream);
 }
 
 int psw_lse_combine(const void* const* partial_out, const float* const* partial_lse,
@@ -286,6 +316,116 @@ int psw_lse_combine(const void* const* partial_out, const float* const* partial_
                                            num_rows, head_dim_v, out, out_dtype == PSW_F32,
                                            out_lse, (hipStream_t)stream),
                    "lse_combine");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Fork and join events of psw_decode_two_streams, made once per device on its
+// first call there and kept until the process ends.  The mutex makes the
+// record / wait sequence of one call atomic with respect to other threads.
+constexpr int kMaxDevices = 64;
+std::mutex g_events_mutex;
+hipEvent_t g_fork[kMaxDevices], g_join[kMaxDevices];
+
+int device_events(hipEvent_t& fork, hipEvent_t& join) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(PSW_ERR_HIP, "no current device below %d", kMaxDevices);
+  if (g_fork[dev] == nullptr) {
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess)
+      return check_hip(hipGetLastError(), "hipEventCreateWithFlags");
+    if (hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+      (void)hipEventDestroy(f);
+      return check_hip(hipGetLastError(), "hipEventCreateWithFlags");
+    }
+    g_fork[dev] = f;
+    g_join[dev] = j;
+  }
+  fork = g_fork[dev];
+  join = g_join[dev];
+  return PSW_OK;
+}
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (a == nullptr || b == nullptr || na <= 0 || nb <= 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+}  // namespace
+
+extern "C" {
+
+int psw_decode_two_streams(const psw_attn_args* history, const psw_attn_args* current,
+                           void* out, int32_t out_dtype, float* out_lse, void* main_stream,
+                           void* side_stream) {
+  psw::AttnParams ph{}, pc{};
+  bool latent_h = false, latent_c = false, empty_h = false, empty_c = false;
+  int64_t ws_h = 0, ws_c = 0;
+  int st = prepare_attention(history, ph, latent_h, empty_h, ws_h);
+  if (st != PSW_OK) return st;
+  st = prepare_attention(current, pc, latent_c, empty_c, ws_c);
+  if (st != PSW_OK) return st;
+  if (history->num_tokens != current->num_tokens ||
+      history->num_q_heads != current->num_q_heads || history->head_dim_v != current->head_dim_v)
+    return fail(PSW_ERR_INVALID, "history and current disagree in tokens, query heads or V dim");
+  if (history->out_dtype != current->out_dtype)
+    return fail(PSW_ERR_INVALID, "history and current partials must share one dtype");
+  if (out_dtype != PSW_BF16 && out_dtype != PSW_F32)
+    return fail(PSW_ERR_INVALID, "out_dtype %d unknown", out_dtype);
+  const int num_partials = history->num_splits + current->num_splits;
+  if (num_partials > psw::kMaxPartials)
+    return fail(PSW_ERR_INVALID, "%d partials, at most %d", num_partials, psw::kMaxPartials);
+  const int dv = history->head_dim_v;
+  if (dv % 8 != 0 || dv > 1024)
+    return fail(PSW_ERR_INVALID, "head_dim_v %d must be a multiple of 8 in [8, 1024]", dv);
+  const int64_t rows = (int64_t)history->num_tokens * history->num_q_heads;
+  if (rows == 0) return ok();
+  if (out == nullptr) return fail(PSW_ERR_INVALID, "out is NULL");
+  if (history->lse == nullptr || current->lse == nullptr)
+    return fail(PSW_ERR_INVALID, "both calls must write their LSE");
+
+  // partial s of a call: its out and lse advanced by s slices of rows
+  const void* po[psw::kMaxPartials];
+  const float* pl[psw::kMaxPartials];
+  const size_t elt = history->out_dtype == PSW_F32 ? 4 : 2;
+  int n = 0;
+  for (const psw_attn_args* a : {history, current})
+    for (int s = 0; s < a->num_splits; ++s, ++n) {
+      po[n] = static_cast<const char*>(a->out) + (size_t)s * rows * dv * elt;
+      pl[n] = a->lse + (size_t)s * rows;
+    }
+
+  hipStream_t ms = (hipStream_t)main_stream, ss = (hipStream_t)side_stream;
+  std::lock_guard<std::mutex> lock(g_events_mutex);
+  if (ms == ss) {
+    if (!empty_h && (st = launch_prepared(history, ph, latent_h, ms)) != PSW_OK) return st;
+    if (!empty_c && (st = launch_prepared(current, pc, latent_c, ms)) != PSW_OK) return st;
+  } else {
+    hipEvent_t fork = nullptr, join = nullptr;
+    if ((st = device_events(fork, join)) != PSW_OK) return st;
+    // One workspace used by both calls orders the current call after the
+    // history call's use of it; separate workspaces let the two run together.
+    const bool shared = overlap(history->workspace, ws_h, current->workspace, ws_c);
+    if (!shared && (st = check_hip(hipEventRecord(fork, ms), "hipEventRecord")) != PSW_OK)
+      return st;
+    if (!empty_h && (st = launch_prepared(history, ph, latent_h, ms)) != PSW_OK) return st;
+    if (shared && (st = check_hip(hipEventRecord(fork, ms), "hipEventRecord")) != PSW_OK)
+      return st;
+    if ((st = check_hip(hipStreamWaitEvent(ss, fork, 0), "hipStreamWaitEvent")) != PSW_OK)
+      return st;
+    if (!empty_c && (st = launch_prepared(current, pc, latent_c, ss)) != PSW_OK) return st;
+    if ((st = check_hip(hipEventRecord(join, ss), "hipEventRecord")) != PSW_OK) return st;
+    // with several ranks, the exchange of history partials is enqueued here on
+    // the main stream, overlapping the current call on the side stream
+    if ((st = check_hip(hipStreamWaitEvent(ms, join, 0), "hipStreamWaitEvent")) != PSW_OK)
+      return st;
+  }
+  return psw_lse_combine(po, pl, num_partials, history->out_dtype, rows, dv, out, out_dtype,
+                         out_lse, main_stream);
 }
 
 int psw_vup_projection(const void* x, const void* w_uv, void* out, int32_t num_tokens,

@@ -120,21 +120,14 @@ def _attn_args(q, k_cache, v_cache, block_table, query_start_loc, seq_lens, *, s
     return a
 
 
-def swa_mm_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor],
-                     block_table: torch.Tensor, query_start_loc: torch.Tensor,
-                     seq_lens: torch.Tensor, *, scale: float, window: int, causal: bool,
-                     chunk_size: int = 0, chunk_lookback: int = -1,
-                     mm_ranges: Optional[torch.Tensor] = None,
-                     key_ranges: Optional[torch.Tensor] = None, head_dim_v: Optional[int] = None,
-                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                     out_dtype: torch.dtype = torch.bfloat16, return_lse: bool = False,
-                     num_splits: Optional[int] = None,
-                     workspace: Optional[torch.Tensor] = None, stream=None):
-    """Paged attention; with key_ranges [S, num_seqs, 2] it writes S fp32/bf16
-    partials out[S, N, Hq, Dv] and lse[S, N, Hq]; without key_ranges,
-    num_splits = S > 1 asks for S segmented splits of every query block's tile
-    loop (partials of the same shape).  ``workspace`` (uint8, device) is
-    allocated here when the call needs one and none is given."""
+def _prepare_attention(q, k_cache, v_cache, block_table, query_start_loc, seq_lens, *, scale,
+                       window, causal, chunk_size, chunk_lookback, mm_ranges, key_ranges,
+                       head_dim_v, out, lse, out_dtype, return_lse, num_splits, workspace,
+                       alloc_workspace=True):
+    """Checks and allocations of one attention call; returns its argument struct,
+    out, lse and workspace (tensors the caller keeps alive).  With
+    alloc_workspace False and no workspace given, the struct's workspace_bytes
+    holds the size the call needs and the caller attaches one."""
     _need(q, "q", torch.bfloat16, 3)
     _need(k_cache, "k_cache", torch.bfloat16, 4)
     if v_cache is not None:
@@ -174,16 +167,107 @@ def swa_mm_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[t
                    num_splits=num_splits)
     need = attention_workspace_size(a)
     if need > 0:
+        if workspace is None and not alloc_workspace:
+            a.workspace_bytes = need
+            return a, out, lse, None
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         _need(workspace, "workspace", torch.uint8)
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    return a, out, lse, workspace
+
+
+def swa_mm_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor],
+                     block_table: torch.Tensor, query_start_loc: torch.Tensor,
+                     seq_lens: torch.Tensor, *, scale: float, window: int, causal: bool,
+                     chunk_size: int = 0, chunk_lookback: int = -1,
+                     mm_ranges: Optional[torch.Tensor] = None,
+                     key_ranges: Optional[torch.Tensor] = None, head_dim_v: Optional[int] = None,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     out_dtype: torch.dtype = torch.bfloat16, return_lse: bool = False,
+                     num_splits: Optional[int] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None):
+    """Paged attention; with key_ranges [S, num_seqs, 2] it writes S fp32/bf16
+    partials out[S, N, Hq, Dv] and lse[S, N, Hq]; without key_ranges,
+    num_splits = S > 1 asks for S segmented splits of every query block's tile
+    loop (partials of the same shape).  ``workspace`` (uint8, device) is
+    allocated here when the call needs one and none is given."""
+    a, out, lse, workspace = _prepare_attention(
+        q, k_cache, v_cache, block_table, query_start_loc, seq_lens, scale=scale, window=window,
+        causal=causal, chunk_size=chunk_size, chunk_lookback=chunk_lookback, mm_ranges=mm_ranges,
+        key_ranges=key_ranges, head_dim_v=head_dim_v, out=out, lse=lse, out_dtype=out_dtype,
+        return_lse=return_lse, num_splits=num_splits, workspace=workspace)
     check(load().psw_swa_mm_attention(ctypes.byref(a), _stream(stream)))
+    n, hq, dv, num_splits = q.shape[0], q.shape[1], a.head_dim_v, a.num_splits
     if key_ranges is None and num_splits == 1:
-        out = out.view(n, hq, head_dim_v)
+        out = out.view(n, hq, dv)
         if lse is not None:
             lse = lse.view(n, hq)
     return (out, lse) if (return_lse or num_splits > 1) else out
+
+
+def decode_two_streams(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor],
+                       block_table: torch.Tensor, query_start_loc: torch.Tensor,
+                       seq_lens: torch.Tensor, *, history_ranges: torch.Tensor,
+                       current_ranges: torch.Tensor, side_stream: torch.cuda.Stream,
+                       scale: float, window: int = 0, causal: bool = True,
+                       head_dim_v: Optional[int] = None,
+                       partial_dtype: torch.dtype = torch.bfloat16,
+                       out_dtype: torch.dtype = torch.bfloat16,
+                       history_workspace: Optional[torch.Tensor] = None,
+                       current_workspace: Optional[torch.Tensor] = None,
+                       shared_workspace: bool = False,
+                       out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
+                       stream=None):
+    """History partials over ``history_ranges`` on the main stream, the current
+    partial over ``current_ranges`` on ``side_stream``, joined and merged by the
+    LSE combine on the main stream (psw_decode_two_streams).  One workspace for
+    both calls (``shared_workspace``, or one tensor passed as both) orders the
+    current call after the history call; separate ones let them overlap.
+    Returns (out [N * Hq, Dv], out_lse [N * Hq], (history out, lse), (current out, lse))."""
+    main = torch.cuda.current_stream() if stream is None else stream
+    if side_stream is None:
+        raise ValueError("side_stream is required")
+    common = dict(scale=scale, window=window, causal=causal, chunk_size=0, chunk_lookback=-1,
+                  mm_ranges=None, head_dim_v=head_dim_v, out=None, lse=None,
+                  out_dtype=partial_dtype, return_lse=True, num_splits=None)
+    alloc = not shared_workspace
+    if shared_workspace and (history_workspace is not None or current_workspace is not None):
+        raise ValueError("shared_workspace allocates the one workspace itself")
+    ah, ho, hl, hw = _prepare_attention(q, k_cache, v_cache, block_table, query_start_loc,
+                                        seq_lens, key_ranges=history_ranges,
+                                        workspace=history_workspace, alloc_workspace=alloc,
+                                        **common)
+    ac, co, cl, cw = _prepare_attention(q, k_cache, v_cache, block_table, query_start_loc,
+                                        seq_lens, key_ranges=current_ranges,
+                                        workspace=current_workspace, alloc_workspace=alloc,
+                                        **common)
+    if shared_workspace:
+        need = max(ah.workspace_bytes, ac.workspace_bytes)
+        if need > 0:
+            hw = cw = torch.empty(need, dtype=torch.uint8, device=q.device)
+            for a in (ah, ac):
+                a.workspace, a.workspace_bytes = hw.data_ptr(), hw.numel()
+    rows, dv = q.shape[0] * q.shape[1], ah.head_dim_v
+    if out is None:
+        out = torch.empty((rows, dv), dtype=out_dtype, device=q.device)
+    _need(out, "out", out_dtype)
+    if out.numel() != rows * dv:
+        raise ValueError("out has the wrong size")
+    if out_lse is None:
+        out_lse = torch.empty(rows, dtype=torch.float32, device=q.device)
+    _need(out_lse, "out_lse", torch.float32)
+    if out_lse.numel() != rows:
+        raise ValueError("out_lse has the wrong size")
+    # tensors the side stream reads or writes stay allocated until it has passed them
+    for t in (q, k_cache, v_cache, block_table, query_start_loc, seq_lens, current_ranges, co, cl,
+              cw):
+        if t is not None:
+            t.record_stream(side_stream)
+    odt = {torch.bfloat16: PSW_BF16, torch.float32: PSW_F32}[out_dtype]
+    check(load().psw_decode_two_streams(ctypes.byref(ah), ctypes.byref(ac), _ptr(out), odt,
+                                        _ptr(out_lse), main.cuda_stream, side_stream.cuda_stream))
+    return out, out_lse, (ho, hl), (co, cl)
 
 
 def attention_workspace_size(args: PswAttnArgs) -> int:

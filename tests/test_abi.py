@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     lib = psw.load()
-    assert lib.psw_abi_version() == 3
+    assert lib.psw_abi_version() == 4
     assert lib.psw_status_string(PSW_OK) == b"ok"
     assert lib.psw_status_string(PSW_ERR_INVALID) == b"invalid argument"
 
@@ -89,8 +89,9 @@ def test_other_entry_points_reject_bad_scalars():
 
 
 def _latent_decode_args(**kw):
-    return _args(num_seqs=4, num_tokens=4, num_q_heads=128, num_kv_heads=1, head_dim_qk=576,
-                 head_dim_v=512, block_size=64, **kw)
+    base = dict(num_seqs=4, num_tokens=4, num_q_heads=128, num_kv_heads=1, head_dim_qk=576,
+                head_dim_v=512, block_size=64)
+    return _args(**{**base, **kw})
 
 
 def test_workspace_size_query():
@@ -125,3 +126,41 @@ def test_latent_decode_rejects_missing_or_small_workspace():
     assert lib.psw_swa_mm_attention(ctypes.byref(small), None) == PSW_ERR_INVALID
     misaligned = _latent_decode_args(workspace=fake + 16, workspace_bytes=n.value, **ptrs)
     assert lib.psw_swa_mm_attention(ctypes.byref(misaligned), None) == PSW_ERR_INVALID
+
+
+def test_two_stream_decode_checks_both_calls_before_enqueuing():
+    # every failure below is found on the host; no pointer is dereferenced
+    lib = psw.load()
+    fake = 0x100000
+    ptrs = dict(q=fake, k_cache=fake, block_table=fake, query_start_loc=fake, seq_lens=fake,
+                out=fake, lse=fake, key_ranges=fake)
+    n = ctypes.c_int64()
+    probe = _latent_decode_args(num_splits=2, **ptrs)
+    assert lib.psw_attention_workspace_size(ctypes.byref(probe), ctypes.byref(n)) == PSW_OK
+    ws = dict(workspace=fake, workspace_bytes=n.value)
+    hist = _latent_decode_args(num_splits=2, **ptrs, **ws)
+    cur = _latent_decode_args(num_splits=1, **ptrs, **ws)
+
+    def call(h, c, out=fake, out_dtype=0):
+        return lib.psw_decode_two_streams(ctypes.byref(h), ctypes.byref(c), out, out_dtype, None,
+                                          None, None)
+    other = dict(ptrs, lse=None)
+    assert call(hist, _latent_decode_args(num_splits=1, **other, **ws)) == PSW_ERR_INVALID
+    assert b"LSE" in lib.psw_last_error()
+    assert call(hist, _latent_decode_args(num_splits=1, num_q_heads=64, **ptrs, **ws)) \
+        == PSW_ERR_INVALID
+    assert b"disagree" in lib.psw_last_error()
+    assert call(hist, _latent_decode_args(num_splits=1, out_dtype=1, **ptrs, **ws)) \
+        == PSW_ERR_INVALID
+    assert call(hist, cur, out=None) == PSW_ERR_INVALID
+    assert call(hist, cur, out_dtype=7) == PSW_ERR_INVALID
+    big = dict(workspace=fake, workspace_bytes=1 << 40)
+    assert call(_latent_decode_args(num_splits=40, **ptrs, **big),
+                _latent_decode_args(num_splits=30, **ptrs, **big)) == PSW_ERR_INVALID
+    assert b"partials" in lib.psw_last_error()
+    no_ws = _latent_decode_args(num_splits=1, **ptrs)
+    assert call(hist, no_ws) == PSW_ERR_INVALID
+    assert b"workspace" in lib.psw_last_error()
+    # an empty batch has nothing to enqueue
+    empty = _args()
+    assert call(empty, empty) == PSW_OK

@@ -47,20 +47,8 @@ def test_mla_decode_full_size():
 
 @pytest.mark.parametrize("seed", range(4))
 def test_small_latent_decode_bf16_partials(seed):
-    from workloads.synth import decode_split_ranges
-    w = make_small_case(900 + seed, num_seqs=5, max_len=3000, hq=64, hkv=1, d=576, dv=512,
-                        window=0, causal=True, chunk=(0, -1), max_ranges=0, latent=True,
-                        block_size=64)
-    # one new token per request: keep only the last position of each request
-    qsl = np.arange(w.num_seqs + 1, dtype=np.int32)
-    last = w.query_start_loc[1:] - 1
-    w.q_bits = w.q_bits[last]
-    w.positions = (w.seq_lens - 1).astype(np.int64)
-    w.context_lens = w.seq_lens - 1
-    w.query_lens = np.ones(w.num_seqs, dtype=np.int64)
-    w.query_start_loc = qsl
-    w.key_ranges = decode_split_ranges(w.seq_lens, 4)
-    w.current_ranges = np.stack([np.stack([w.seq_lens - 1, w.seq_lens], 1)]).astype(np.int32)
+    # one new token per request: the last position of each request
+    w = _small_decode_case(900 + seed)
     gw = GpuWorkload(w)
     out, lse, *_ = _decode(gw, w, partial_dtype=torch.bfloat16)
     out = out.float().cpu().numpy().reshape(w.num_tokens, w.num_q_heads, w.head_dim_v)
@@ -148,3 +136,69 @@ def test_latent_decode_scheduling(case):
             ref_o, ref_l = oracle_rows(w, r, key_range=tuple(w.key_ranges[j, r]))
             assert_close(ho[j, t0:t1], ref_o, f"split {j} of request {r}")
             assert_lse_close(hl[j, t0:t1], ref_l, f"split {j} of request {r} lse")
+
+
+def _small_decode_case(seed, num_seqs=5, splits=4):
+    from workloads.synth import decode_split_ranges
+    w = make_small_case(seed, num_seqs=num_seqs, max_len=3000, hq=64, hkv=1, d=576, dv=512,
+                        window=0, causal=True, chunk=(0, -1), max_ranges=0, latent=True,
+                        block_size=64)
+    last = w.query_start_loc[1:] - 1
+    w.q_bits = w.q_bits[last]
+    w.positions = (w.seq_lens - 1).astype(np.int64)
+    w.context_lens = w.seq_lens - 1
+    w.query_lens = np.ones(w.num_seqs, dtype=np.int64)
+    w.query_start_loc = np.arange(w.num_seqs + 1, dtype=np.int32)
+    w.key_ranges = decode_split_ranges(w.seq_lens, splits)
+    w.current_ranges = np.stack([np.stack([w.seq_lens - 1, w.seq_lens], 1)]).astype(np.int32)
+    return w
+
+
+@pytest.mark.parametrize("case", ["full", "small"])
+@pytest.mark.parametrize("shared", [False, True])
+def test_two_stream_decode(case, shared):
+    """History partials on the main stream, the current partial on a side
+    stream, joined before the LSE combine ([DCP] 2.1 stream swap, 3.2, blocks C
+    and D): bit-identical to the same three calls in order on one stream, with
+    the current call overlapping the history call (separate workspaces) or
+    ordered after it (one shared workspace), over repeated calls with other
+    work in between; and the merged rows equal the oracle."""
+    w = make_config(5) if case == "full" else _small_decode_case(950)
+    gw = GpuWorkload(w)
+    ref_out, ref_lse, ref_ho, ref_hl, ref_co, ref_cl = _decode(gw, w, partial_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    hr, cr = i32(w.key_ranges), i32(w.current_ranges)
+    for rep in range(3):
+        out, lse, (ho, hl), (co, cl) = psw.decode_two_streams(
+            gw.q, gw.k_cache, None, gw.block_table, gw.qsl, gw.seq_lens, history_ranges=hr,
+            current_ranges=cr, side_stream=side, scale=w.scale, window=w.window, causal=w.causal,
+            head_dim_v=w.head_dim_v, partial_dtype=torch.bfloat16, shared_workspace=shared)
+        torch.cuda.synchronize()
+        for name, got, ref in (("out", out, ref_out), ("lse", lse, ref_lse), ("history", ho, ref_ho),
+                               ("history lse", hl, ref_hl), ("current", co, ref_co),
+                               ("current lse", cl, ref_cl)):
+            assert torch.equal(got.view(-1), ref.view(-1)), f"{name} differs on call {rep}"
+        # unrelated eager work on the main stream between calls
+        torch.randn(1 << 20, device="cuda").sum().item()
+    out = out.float().cpu().numpy().reshape(w.num_tokens, w.num_q_heads, w.head_dim_v)
+    lse = lse.cpu().numpy().reshape(w.num_tokens, w.num_q_heads)
+    for r in ((0, 31, 63) if case == "full" else range(w.num_seqs)):
+        ref_o, ref_l = oracle_rows(w, r)
+        assert_close(out[r], ref_o[0], f"token {r}")
+        assert_lse_close(lse[r], ref_l[0], f"token {r} lse")
+
+
+def test_two_stream_decode_on_one_stream():
+    """main stream == side stream: the three steps in order on that stream."""
+    w = _small_decode_case(951, num_seqs=3, splits=2)
+    gw = GpuWorkload(w)
+    ref_out, ref_lse, *_ = _decode(gw, w, partial_dtype=torch.bfloat16)
+    main = torch.cuda.current_stream()
+    out, lse, _, _ = psw.decode_two_streams(
+        gw.q, gw.k_cache, None, gw.block_table, gw.qsl, gw.seq_lens,
+        history_ranges=i32(w.key_ranges), current_ranges=i32(w.current_ranges), side_stream=main,
+        scale=w.scale, window=w.window, causal=w.causal, head_dim_v=w.head_dim_v,
+        partial_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(-1), ref_out.view(-1)) and torch.equal(lse, ref_lse)
