@@ -15,7 +15,8 @@
  *     alive until the enqueued work has finished. Arrays of pointers and the
  *     argument struct itself are HOST memory, read before the call returns.
  *   - `stream` is a hipStream_t (NULL: the legacy default stream). Every call
- *     only enqueues work on it: no allocation, no host synchronisation.
+ *     only enqueues work on it: no device allocation, no host synchronisation
+ *     (psw_decode_two_streams also creates two HIP events per device, once).
  *   - Scalars and pointer presence are validated on the host. On any error
  *     nothing is enqueued and outputs are untouched. Device-resident data
  *     (offsets, positions, table entries) is NOT validated; the preconditions
