@@ -459,7 +459,6 @@ def bench_decode(args, torch, psw, np):
     two = bench_two_streams(torch, psw, np, w, q, cache, bt, qsl, seq_lens, kr_all, S, pdt, out,
                             one_call)
     return {
-        "two_streams": two,
         "workload": "mla_splitkv_decode_b64",
         "unit": "GB/s",
         "value": round(gbs, 1),
@@ -477,6 +476,7 @@ def bench_decode(args, torch, psw, np):
         "partial_dtype": args.decode_partials,
         "step": "slot_mapping + kv_cache_write + history and current partials (one call) "
                 "+ lse_combine + vup_projection",
+        "two_streams": two,
     }
 
 
