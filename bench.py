@@ -28,6 +28,19 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 
 
+def warm(torch, fn, min_ms=100.0, min_calls=3):
+    """Untimed calls of fn until at least min_ms of wall time has passed, so a
+    timing taken after a host-side pause starts at steady clocks."""
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while n < min_calls or (time.perf_counter() - t0) * 1e3 < min_ms:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -36,7 +49,10 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the GPU's clocks ramp up over the first ~25 ms of sustained load (a
+    # 16,550-token prefill launch drops from 0.48 to 0.37 ms over its first ~60
+    # launches, and climbs back after 2 s idle): 200 steps are ~100 ms
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--skip-decode", action="store_true", help="omit the decode half")
     ap.add_argument("--decode-splits", type=int, default=1)
@@ -270,9 +286,7 @@ def bench_segmented(torch, psw, splits=4, reps=20):
 
     res = {"workload": "noncausal_chunk_lookback_2x4096", "splits": splits}
     for name, fn in (("unsplit_ms", unsplit), ("segmented_with_combine_ms", segmented)):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
+        warm(torch, fn)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
@@ -308,9 +322,7 @@ def bench_slot_mapping(torch, psw, np, num_reqs=4096, seed=7):
     m = n + 65536
     d_qsl, d_pos, d_bt = i32(qsl), i64(pos), i32(bt)
     out = torch.empty(m, dtype=torch.int32, device="cuda")
-    for _ in range(3):
-        psw.slot_mapping(d_qsl, d_pos, d_bt, B, m, out=out)
-    torch.cuda.synchronize()
+    warm(torch, lambda: psw.slot_mapping(d_qsl, d_pos, d_bt, B, m, out=out))
     reps = 50
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -340,9 +352,7 @@ def bench_slot_mapping(torch, psw, np, num_reqs=4096, seed=7):
     def run_cp():
         psw.slot_mapping_cp(d_qsl, d_pos, d_bt_cp, B, m, kv_cache_block_size=kvb,
                             cp_world_size=world, cp_rank=rank, cp_interleave=inter, out=out)
-    for _ in range(3):
-        run_cp()
-    torch.cuda.synchronize()
+    warm(torch, run_cp)
     e0.record()
     for _ in range(reps):
         run_cp()
@@ -526,6 +536,8 @@ def bench_two_streams(torch, psw, np, w, q, cache, bt, qsl, seq_lens, kr_all, S,
                 "two_streams_separate_workspaces_ms": streams(False),
                 "two_streams_shared_workspace_ms": streams(True)}
     times = {k: [] for k in variants}
+    for fn in variants.values():
+        warm(torch, fn, min_ms=30.0)
     for _ in range(rounds):
         for k, fn in variants.items():
             times[k].append(timed(fn))
