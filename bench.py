@@ -436,6 +436,18 @@ def bench_decode(args, torch, psw, np):
         if i is not None:
             ev[i][3].record()
 
+    def one_call():
+        psw.swa_mm_attention(q, cache, None, bt, qsl, seq_lens, scale=w.scale, window=0,
+                             causal=True, key_ranges=kr_all, head_dim_v=DV, out=part_o,
+                             lse=part_l, out_dtype=pdt, workspace=ws)
+        psw.lse_combine(outs, lses, out=out)
+
+    # first, so that the decode kernel's last launches are the timed steps below;
+    # one step writes the current keys into the cache
+    step()
+    log("timing decode on two streams")
+    two = bench_two_streams(torch, psw, np, w, q, cache, bt, qsl, seq_lens, kr_all, S, pdt, out,
+                            one_call)
     log("timing decode")
     for _ in range(args.warmup):
         step()
@@ -459,15 +471,6 @@ def bench_decode(args, torch, psw, np):
                  + vup_out.numel() * 2)
     gbs = alg_bytes / (ms * 1e-3) / 1e9
     attn_gbs = (kv_bytes + q.numel() * 2) / (attn_ms * 1e-3) / 1e9
-    def one_call():
-        psw.swa_mm_attention(q, cache, None, bt, qsl, seq_lens, scale=w.scale, window=0,
-                             causal=True, key_ranges=kr_all, head_dim_v=DV, out=part_o,
-                             lse=part_l, out_dtype=pdt, workspace=ws)
-        psw.lse_combine(outs, lses, out=out)
-
-    log("timing decode on two streams")
-    two = bench_two_streams(torch, psw, np, w, q, cache, bt, qsl, seq_lens, kr_all, S, pdt, out,
-                            one_call)
     return {
         "workload": "mla_splitkv_decode_b64",
         "unit": "GB/s",
