@@ -335,11 +335,12 @@ int device_events(hipEvent_t& fork, hipEvent_t& join) {
     return fail(PSW_ERR_HIP, "no current device below %d", kMaxDevices);
   if (g_fork[dev] == nullptr) {
     hipEvent_t f = nullptr, j = nullptr;
-    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess)
-      return check_hip(hipGetLastError(), "hipEventCreateWithFlags");
-    if (hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+    hipError_t e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+    if (e != hipSuccess) return check_hip(e, "hipEventCreateWithFlags");
+    e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+    if (e != hipSuccess) {
       (void)hipEventDestroy(f);
-      return check_hip(hipGetLastError(), "hipEventCreateWithFlags");
+      return check_hip(e, "hipEventCreateWithFlags");
     }
     g_fork[dev] = f;
     g_join[dev] = j;
