@@ -17,8 +17,10 @@
  *   - `stream` is a hipStream_t (NULL: the legacy default stream). Every call
  *     only enqueues work on it: no device allocation, no host synchronisation
  *     (psw_decode_two_streams also creates two HIP events per device, once).
- *   - Scalars and pointer presence are validated on the host. On any error
- *     nothing is enqueued and outputs are untouched. Device-resident data
+ *   - Scalars and pointer presence are validated on the host. When a check
+ *     fails (PSW_ERR_INVALID, PSW_ERR_UNSUPPORTED) nothing is enqueued and
+ *     outputs are untouched; PSW_ERR_HIP means a launch failed, possibly after
+ *     earlier launches of the same call were enqueued. Device-resident data
  *     (offsets, positions, table entries) is NOT validated; the preconditions
  *     listed per call are the caller's to keep.
  *   - All tensors are dense and row-major (last dimension contiguous).
