@@ -26,9 +26,12 @@ def _hipcc():
 
 
 def _kernel_bodies(asm: str, prefix: str):
+    # a kernel's code runs to its .Lfunc_end label: early returns put further
+    # s_endpgm instructions inside the body
     for m in re.finditer(r"^(%s\w*):" % re.escape(prefix), asm, re.M):
-        end = asm.index("s_endpgm", m.end())
-        yield m.group(1), asm[m.end():end]
+        end = asm.index(".Lfunc_end", m.end())
+        body = asm[m.end():end]
+        yield m.group(1), body
 
 
 @pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
@@ -57,5 +60,16 @@ def test_full_width_decode_leaves_agprs_to_inline_asm(tmp_path):
             code = t.split(";")[0]
             assert not re.search(r"\ba\d+\b|\ba\[\d+", code), f"{name}: compiler AGPR use: {t}"
         assert "scratch_" not in body, f"{name}: register spills"
+        # the whole kernel was searched: its main loop has the output MFMAs
+        assert body.count("v_mfma") >= 16 and body.count("s_endpgm") >= 1, name
     # the kernel descriptors reserve all 256 AGPRs (the clobber of a255)
     assert len(re.findall(r"\.agpr_count:\s+256", asm)) >= 2
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The bench measures one GPU; asking for more ends with a message and a
+    non-zero status before any GPU work."""
+    r = subprocess.run([os.environ.get("PYTHON", "python3"), os.path.join(ROOT, "bench.py"),
+                        "--gpus", "2"], capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode != 0
+    assert "one GPU only" in r.stdout + r.stderr
