@@ -20,7 +20,7 @@ def pytest_collection_modifyitems(config, items):
 
 @pytest.fixture(autouse=True)
 def _gpu_guard(request):
-    """GPU tests need a visible GPU; on a GPU machine a missing library still fails loudly."""
+    """GPU tests need a visible GPU; where one is visible, a missing library still fails loudly."""
     if request.node.get_closest_marker("gpu") is not None:
         import torch
         if not torch.cuda.is_available():
