@@ -385,6 +385,9 @@ int psw_decode_two_streams(const psw_attn_args* history, const psw_attn_args* cu
     return fail(PSW_ERR_INVALID, "head_dim_v %d must be a multiple of 8 in [8, 1024]", dv);
   const int64_t rows = (int64_t)history->num_tokens * history->num_q_heads;
   if (rows == 0) return ok();
+  if (history->num_seqs == 0 || current->num_seqs == 0)
+    return fail(PSW_ERR_INVALID, "%d tokens but no sequences: the combine would read unwritten "
+                "partials", history->num_tokens);
   if (out == nullptr) return fail(PSW_ERR_INVALID, "out is NULL");
   if (history->lse == nullptr || current->lse == nullptr)
     return fail(PSW_ERR_INVALID, "both calls must write their LSE");

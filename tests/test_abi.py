@@ -161,6 +161,8 @@ def test_two_stream_decode_checks_both_calls_before_enqueuing():
     no_ws = _latent_decode_args(num_splits=1, **ptrs)
     assert call(hist, no_ws) == PSW_ERR_INVALID
     assert b"workspace" in lib.psw_last_error()
+    assert call(hist, _latent_decode_args(num_splits=1, num_seqs=0, **ptrs, **ws)) == PSW_ERR_INVALID
+    assert b"no sequences" in lib.psw_last_error()
     # an empty batch has nothing to enqueue
     empty = _args()
     assert call(empty, empty) == PSW_OK
