@@ -272,7 +272,8 @@ int psw_lse_combine(const void* const* partial_out, const float* const* partial_
  *             num_q_heads and head_dim_v of the two calls
  * Both calls are checked exactly as psw_swa_mm_attention checks one; they must
  * agree in num_tokens, num_q_heads, head_dim_v and out_dtype (the partial
- * dtype), both must write lse, and together hold at most 64 partials.  The
+ * dtype), both must write lse and, with tokens, have sequences, and together
+ * hold at most 64 partials.  The
  * combine reads history's partials 0 .. S_h - 1 and then current's, in place.
  * Ordering: the side stream waits for an event recorded on main_stream, either
  * before the history call (the two workspaces are disjoint: the current call
