@@ -5,27 +5,39 @@ multimodal prefill (16,550 tokens, 60 images of 256 tokens, W 1024, 16 query /
 8 KV heads, head dim 256, paged in blocks of 16):
   slot mapping of the new tokens -> KV-cache write -> paged prefill attention.
 The decode half of the path (MLA-shaped split-KV decode: 64 requests, 128 heads,
-576/512 latent, history partial(s) + the current key's partial from one call,
-LSE combine) is timed in the same run and reported under "decode".
+576/512 latent, history partial + the current key's partial from one call,
+LSE combine, V-up projection) is timed in the same run and reported under
+"decode"; the other prefill workloads (tiny, batched chunked, non-causal chunk
+lookback) under "prefill_configs".
 
 Reported value: algorithmic TFLOP/s = 4 * head_dim FLOP per allowed
-(query, key, head) triple, 3.0115e11 per step, over the measured step time.
-The "roofline" object is for the dominant kernel (prefill attention), timed
-with HIP events around each of its launches on the stream it runs on.
+(query, key, head) triple over the measured step time.  The "roofline" object
+is for the dominant kernel (prefill attention), timed with HIP events around
+each of its launches on the stream it runs on, after a time-based warm-up that
+brings the clocks to their steady state.
 """
 from __future__ import annotations
 
-import argparse
-import json
 import os
-import sys
-import time
+
+# BLAS / OpenMP threads of the CPU-baseline leg: the cores this process may
+# run on, fixed before numpy is first imported (an explicit setting wins)
+_CORES = len(os.sched_getaffinity(0))
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_v, str(_CORES))
+
+import argparse  # noqa: E402
+import json  # noqa: E402
+import subprocess  # noqa: E402
+import sys  # noqa: E402
+import time  # noqa: E402
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+METRIC = "SWA+MM-prefix prefill attn TFLOP/s (% MFMA peak); paged decode HBM GB/s"
 
 
 def warm(torch, fn, min_ms=100.0, min_calls=3):
@@ -39,6 +51,7 @@ def warm(torch, fn, min_ms=100.0, min_calls=3):
         if n % 8 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3
 
 
 def log(msg):
@@ -49,14 +62,17 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # the GPU's clocks ramp up over the first ~25 ms of sustained load (a
-    # 16,550-token prefill launch drops from 0.48 to 0.37 ms over its first ~60
-    # launches, and climbs back after 2 s idle): 200 steps are ~100 ms
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warm-ms", type=float, default=200.0,
+                    help="time-based warm-up before each timed section, on top of --warmup "
+                         "steps: the clocks ramp up over the first ~25 ms of sustained load "
+                         "and drop again after a pause")
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU oracle baseline")
     ap.add_argument("--skip-decode", action="store_true", help="omit the decode half")
+    ap.add_argument("--skip-extra", action="store_true",
+                    help="omit everything but the headline step and the decode step")
     ap.add_argument("--decode-splits", type=int, default=1)
-    ap.add_argument("--decode-partials", choices=["f32", "bf16"], default="bf16",
+    ap.add_argument("--decode-partials", choices=["f32", "bf16", "f16"], default="bf16",
                     help="dtype of the history/current partial outputs")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="first run one plain device copy of this many bytes (a known-size "
@@ -64,54 +80,161 @@ def parse():
     return ap.parse_args()
 
 
-def allowed_pairs_per_head(w, r):
-    """Allowed (query, key) pairs of request r for one head: each causal row's
-    allowed keys form one interval (window part and image part both contain the
-    query position), so the count is the interval length."""
-    total = 0
-    ctx = int(w.context_lens[r])
-    L = int(w.seq_lens[r])
-    ranges = [(s, e) for s, e in w.ranges_of(r) if s < e]
-    W = w.window
-    for i in range(int(w.query_lens[r])):
-        q = ctx + i
-        lo = max(0, q - W + 1) if W > 0 else 0
-        hi = q
-        for s, e in ranges:
-            if s <= q <= e:
-                lo = min(lo, max(s, q - W + 1) if W > 0 else s)
-                hi = max(hi, e)
-        total += min(hi, L - 1) - lo + 1
-    return total
+# ---- algorithmic work ---------------------------------------------------------
+
+def allowed_pairs(w, r, rows=None):
+    """Allowed (query, key) pairs of request r for one head, from the mask's
+    definition: each row's allowed keys form one interval containing the query
+    position (base window, optionally cut by the chunk-lookback edge, united
+    with every image range that holds the query, clamped on the left by the
+    window), so the count is the interval length, clamped to [0, seq_len)."""
+    import numpy as np
+    ctx, L, W = int(w.context_lens[r]), int(w.seq_lens[r]), w.window
+    i = np.arange(int(w.query_lens[r]), dtype=np.int64) if rows is None else np.asarray(rows)
+    q = ctx + i
+    if w.causal:
+        lo = q - W + 1 if W > 0 else np.zeros_like(q)
+        hi = q.copy()
+    else:
+        lo = q - W + 1 if W > 0 else np.zeros_like(q)
+        hi = q + W - 1 if W > 0 else np.full_like(q, L - 1)
+    if w.chunk_lookback >= 0:
+        lo = np.maximum(lo, (q // w.chunk_size - w.chunk_lookback) * w.chunk_size)
+    for s, e in w.ranges_of(r):
+        if s < e:
+            inside = (q >= s) & (q <= e)
+            img_lo = np.maximum(s, q - W + 1) if W > 0 else np.full_like(q, s)
+            lo = np.where(inside, np.minimum(lo, img_lo), lo)
+            hi = np.where(inside, np.maximum(hi, e), hi)
+    lo, hi = np.maximum(lo, 0), np.minimum(hi, L - 1)
+    return int(np.maximum(hi - lo + 1, 0).sum())
 
 
 def prefill_flop(w):
-    pairs = sum(allowed_pairs_per_head(w, r) for r in range(w.num_seqs))
+    pairs = sum(allowed_pairs(w, r) for r in range(w.num_seqs))
     return pairs * w.num_q_heads * 4 * w.head_dim_qk, pairs
 
 
-def cpu_baseline(w):
-    """The oracle (as written) on the whole prefill workload, repeated until at
-    least 10 s of CPU time have been spent (at most 5 passes)."""
+def timed_events(torch, fn, reps, rounds=5):
+    """Median over `rounds` of the mean event time of `reps` back-to-back calls (ms)."""
+    import numpy as np
+    out = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / reps)
+    return float(np.median(out))
+
+
+# ---- CPU baseline (the oracle as written, on this host's cores) --------------
+
+def cpu_model():
+    try:
+        txt = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in txt.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return "unknown"
+
+
+def cpu_baseline(budget_s=45.0):
+    """The oracle legs per workload: dense masked attention (O4), the tile-pruned
+    attention (O5, the method on the CPU), scalar slot mapping (O1) and the LSE
+    merge (O7); best of up to 3 passes while the leg's single pass is short,
+    within an overall time budget."""
+    import numpy as np
     from threadpoolctl import threadpool_info
 
-    from oracle import attention_ref
-    q = w.q_f32()
-    k, v = w.k_f32(0), w.v_f32(0)
-    flop, _ = prefill_flop(w)
-    passes, t0 = 0, time.perf_counter()
-    while True:
-        attention_ref(q, k, v, context_len=0, seq_len=int(w.seq_lens[0]), scale=w.scale,
-                      window=w.window, causal=w.causal, ranges=w.ranges_of(0))
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or passes >= 5:
-            break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(flop * passes / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"float64 numpy oracle over the whole 16,550-token prefill (all 16 heads), "
-                      f"{passes} pass(es) in {dt:.2f} s"}
+    from oracle import attention_pruned_ref, attention_ref, lse_merge_ref, slot_mapping_ref
+    from workloads import make_config
+
+    t_start = time.perf_counter()
+
+    def best(fn, max_passes=3):
+        times = []
+        while len(times) < max_passes:
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+            if times[-1] > 2.0 or time.perf_counter() - t_start > budget_s:
+                break
+        return min(times), len(times)
+
+    def attn_leg(w, fn_name, rows_limit=None, seqs_limit=None):
+        fn = attention_ref if fn_name == "O4" else attention_pruned_ref
+        q_all = w.q_f32()
+        flop = 0
+        calls = []
+        for r in range(w.num_seqs if seqs_limit is None else seqs_limit):
+            s0, s1 = int(w.query_start_loc[r]), int(w.query_start_loc[r + 1])
+            n = s1 - s0 if rows_limit is None else min(rows_limit, s1 - s0)
+            flop += allowed_pairs(w, r, rows=np.arange(n)) * w.num_q_heads * 4 * w.head_dim_qk
+            kw = dict(context_len=int(w.context_lens[r]), seq_len=int(w.seq_lens[r]),
+                      scale=w.scale, window=w.window, causal=w.causal, chunk_size=w.chunk_size,
+                      chunk_lookback=w.chunk_lookback, ranges=w.ranges_of(r))
+            calls.append((q_all[s0:s0 + n], w.k_f32(r), w.v_f32(r), kw))
+
+        def run():
+            for q, k, v, kw in calls:
+                fn(q, k, v, **kw)
+        t, n_pass = best(run)
+        return {"TFLOPs": round(flop / t / 1e12, 6), "s": round(t, 4), "passes": n_pass,
+                "flop": flop}
+
+    def slot_leg(w):
+        byts = w.num_tokens * 12 + (w.max_num_tokens - w.num_tokens) * 4
+        t, n_pass = best(lambda: slot_mapping_ref(w.query_start_loc, w.positions, w.block_table,
+                                                  w.block_size, w.max_num_tokens))
+        return {"GBps": round(byts / t / 1e9, 6), "s": round(t, 5), "passes": n_pass}
+
+    legs = {}
+    threads = None
+    for cfg in (2, 1, 5, 3, 4):
+        if time.perf_counter() - t_start > budget_s:
+            legs[f"config{cfg}"] = "skipped: time budget"
+            continue
+        w = make_config(cfg)
+        d = {"workload": w.name}
+        if cfg == 5:
+            # the decode's dense oracle over every key of each request, and the
+            # merge of its two partials' shape (64 x 128 rows of 512)
+            d["O4_dense_decode_first_16_requests"] = attn_leg(w, "O4", seqs_limit=16)
+            rng = np.random.default_rng(5)
+            rows = w.num_tokens * w.num_q_heads
+            outs = [rng.standard_normal((rows, w.head_dim_v)).astype(np.float32) for _ in range(2)]
+            lses = [rng.standard_normal(rows).astype(np.float32) for _ in range(2)]
+            t, n_pass = best(lambda: lse_merge_ref(outs, lses))
+            byts = sum(o.nbytes for o in outs) + sum(x.nbytes for x in lses) + rows * w.head_dim_v * 2
+            d["O7_lse_merge"] = {"GBps": round(byts / t / 1e9, 6), "s": round(t, 5), "passes": n_pass,
+                                 "partials": 2}
+        else:
+            d["O4_dense"] = attn_leg(w, "O4")
+            if cfg in (2, 4):
+                # the pruned pass (a Python loop over query blocks) over the first
+                # 2,048 rows of each request: one eighth / one half of the work
+                d["O5_pruned_first_2048_rows"] = attn_leg(w, "O5", rows_limit=2048)
+            else:
+                d["O5_pruned"] = attn_leg(w, "O5")
+            d["O1_slot_mapping"] = slot_leg(w)
+        legs[f"config{cfg}"] = d
+        if threads is None:
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    head = legs.get("config2", {})
+    value = head["O4_dense"]["TFLOPs"] if isinstance(head, dict) and "O4_dense" in head else None
+    return {"value": value, "unit": "TFLOP/s", "cores": _CORES, "kind": "oracle",
+            "sample": "float64 numpy oracle (dense masked attention) over the whole 16,550-token "
+                      "multimodal prefill, all 16 heads, one pass; per-workload legs below "
+                      "(O4 dense, O5 pruned, O1 slot mapping, O7 LSE merge; best of up to 3 "
+                      "passes)",
+            "blas_threads": threads, "cpu_model": cpu_model(),
+            "affinity_cores": _CORES, "legs": legs,
+            "total_s": round(time.perf_counter() - t_start, 1)}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_attention_gemma16550_traffic.json")
@@ -145,7 +268,7 @@ def main():
     import torch
 
     import paged_sliding_window_amd as psw
-    from tests.gpu_setup import GpuWorkload, bits_to_bf16, i32, i64
+    from tests.gpu_setup import GpuWorkload, bits_to_bf16
     from workloads import make_config
 
     torch.cuda.set_device(0)
@@ -190,7 +313,7 @@ def main():
     log("timing prefill")
     for _ in range(args.warmup):
         prefill_step()
-    torch.cuda.synchronize()
+    warm_ms = warm(torch, prefill_step, min_ms=args.warm_ms)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -205,7 +328,7 @@ def main():
     achieved = flop / (attn_ms * 1e-3) / 1e12
 
     result = {
-        "metric": "SWA+MM-prefix prefill attn TFLOP/s (% MFMA peak); paged decode HBM GB/s",
+        "metric": METRIC,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -226,7 +349,7 @@ def main():
             "step": "slot_mapping + kv_cache_write + swa_mm_attention",
         },
         "roofline": {
-            "kernel": "prefill_attention_kernel<PrefillShape<256, 4, 2>>",
+            "kernel": "prefill attention, head dim 256 (workload 2)",
             "bound": "mfma",
             "achieved": round(achieved, 3),
             "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -234,34 +357,71 @@ def main():
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": measured_traffic(),
             "avg_launch_ms": round(attn_ms, 5),
+            "clock_state": f"steady: {args.warmup} warm-up steps, then {warm_ms:.0f} ms of "
+                           "back-to-back steps before the timed ones",
         },
     }
     del gw, k_new, v_new, out, lse
     torch.cuda.empty_cache()
+    log(f"prefill {ms_per_step:.4f} ms/step, attention {attn_ms:.4f} ms")
 
     # ---------------- decode (second half of the path) ----------------
-    log(f"prefill {ms_per_step:.4f} ms/step, attention {attn_ms:.4f} ms")
     if not args.skip_decode:
         log("decode half")
         result["decode"] = bench_decode(args, torch, psw, np)
-
-    log("segmented splits, non-causal workload")
-    result["prefill_segmented"] = bench_segmented(torch, psw)
-    log("slot mapping, scaled batch")
-    result["slot_mapping_scaled"] = bench_slot_mapping(torch, psw, np)
+    if not args.skip_extra:
+        log("other prefill workloads")
+        result["prefill_configs"] = bench_prefill_configs(args, torch, psw)
+        log("segmented splits, non-causal workload")
+        result["prefill_segmented"] = bench_segmented(args, torch, psw)
+        log("slot mapping, scaled batch")
+        result["slot_mapping_scaled"] = bench_slot_mapping(args, torch, psw, np)
     if not args.skip_cpu:
         log("CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline"] = cpu_baseline()
     result["setup_s"] = round(time.perf_counter() - t_setup, 1)
     print(json.dumps(result), flush=True)
 
 
-def bench_segmented(torch, psw, splits=4, reps=20):
-    """The non-causal chunk-lookback workload (2 x 4,096 tokens, 8 heads, d 128):
-    with 128-row query blocks it has 528 workgroups, one round of the GPU's
-    512 slots plus a few; segmented splits (each block's tile loop cut into
-    `splits` pieces, merged by the LSE combine) spread the same tiles over
-    more, shorter workgroups.  Reports both times; not part of the step."""
+def bench_prefill_configs(args, torch, psw):
+    """Attention alone on the tiny (latency), batched chunked and non-causal
+    chunk-lookback workloads: event-timed median of 5 rounds after a warm-up."""
+    from tests.gpu_setup import GpuWorkload
+    from workloads import make_config
+    res = {}
+    for cfg in (1, 3, 4):
+        w = make_config(cfg)
+        flop, pairs = prefill_flop(w)
+        gw = GpuWorkload(w)
+        out = torch.empty((w.num_tokens, w.num_q_heads, w.head_dim_v), dtype=torch.bfloat16,
+                          device="cuda")
+        lse = torch.empty((w.num_tokens, w.num_q_heads), dtype=torch.float32, device="cuda")
+
+        def fn():
+            psw.swa_mm_attention(gw.q, gw.k_cache, gw.v_cache, gw.block_table, gw.qsl,
+                                 gw.seq_lens, scale=w.scale, window=w.window, causal=w.causal,
+                                 chunk_size=w.chunk_size, chunk_lookback=w.chunk_lookback,
+                                 mm_ranges=gw.mm_ranges, out=out, lse=lse)
+        warm(torch, fn, min_ms=args.warm_ms / 2)
+        ms = timed_events(torch, fn, reps=50 if cfg == 1 else 20)
+        tf = flop / (ms * 1e-3) / 1e12
+        res[w.name] = {"head_dim": w.head_dim_qk, "tokens": w.num_tokens,
+                       "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                       "allowed_pairs_per_head": pairs, "flop": flop,
+                       "attention_ms": round(ms, 5), "TFLOPs": round(tf, 3),
+                       "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        if cfg == 1:
+            res[w.name]["latency_us"] = round(ms * 1e3, 2)
+            res[w.name]["note"] = "launch-latency bound: the fraction of peak is not meaningful"
+        del gw, out, lse
+        torch.cuda.empty_cache()
+    return res
+
+
+def bench_segmented(args, torch, psw, splits=4, reps=20):
+    """The non-causal chunk-lookback workload (2 x 4,096 tokens, 8 heads, d 128)
+    unsplit and with each query block's tile loop cut into `splits` segmented
+    pieces merged by the LSE combine.  Reports both times; not part of the step."""
     from tests.gpu_setup import GpuWorkload
     from workloads import make_config
     w = make_config(4)
@@ -286,192 +446,124 @@ def bench_segmented(torch, psw, splits=4, reps=20):
 
     res = {"workload": "noncausal_chunk_lookback_2x4096", "splits": splits}
     for name, fn in (("unsplit_ms", unsplit), ("segmented_with_combine_ms", segmented)):
-        warm(torch, fn)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        res[name] = round(e0.elapsed_time(e1) / reps, 5)
+        warm(torch, fn, min_ms=args.warm_ms / 4)
+        res[name] = round(timed_events(torch, fn, reps), 5)
     del gw
     torch.cuda.empty_cache()
     return res
 
 
-def bench_slot_mapping(torch, psw, np, num_reqs=4096, seed=7):
-    """Slot mapping over a large synthetic batch (not one of the workloads: at
-    their sizes the kernel moves under 0.3 MB and only latency shows).
-    Algorithmic bytes: 8 B position read + 4 B slot written per token, the
-    block-table entries of the blocks touched, and 4 B per pad slot."""
+def bench_slot_mapping(args, torch, psw, np, num_reqs=20000, seed=7):
+    """Slot mapping over a 41 M-token batch (not one of the workloads: at their
+    sizes the kernel moves under 0.3 MB and only latency shows).  Algorithmic
+    bytes: 8 B position read + 4 B slot written per token, the block-table
+    entries of the blocks touched, and 4 B per pad slot.  For scale, the same
+    run times torch's int64 -> int32 copy of the positions (the same 8 B read
+    and 4 B written per token): the plateau a streaming kernel of this shape
+    reaches on this GPU."""
     from tests.gpu_setup import i32, i64
-    rng = np.random.default_rng(seed)
+    from workloads.synth import make_slot_batch
     B = 16
-    lens = rng.integers(512, 2049, size=num_reqs)
-    need = -(-lens // B)
-    stride = int(need.max())
-    bt = np.full((num_reqs, stride), -1, dtype=np.int32)
-    perm = rng.permutation(int(need.sum())).astype(np.int32)
-    off = 0
-    for r in range(num_reqs):
-        bt[r, :need[r]] = perm[off:off + need[r]]
-        off += need[r]
-    qsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    pos = np.concatenate([np.arange(L) for L in lens]).astype(np.int64)
+    qsl, pos, bt = make_slot_batch(num_reqs, 1024, 3072, B, seed)
     n = int(qsl[-1])
     m = n + 65536
+    need = int((bt >= 0).sum())
     d_qsl, d_pos, d_bt = i32(qsl), i64(pos), i32(bt)
     out = torch.empty(m, dtype=torch.int32, device="cuda")
-    warm(torch, lambda: psw.slot_mapping(d_qsl, d_pos, d_bt, B, m, out=out))
-    reps = 50
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        psw.slot_mapping(d_qsl, d_pos, d_bt, B, m, out=out)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    alg = n * 12 + int(need.sum()) * 4 + (m - n) * 4
+    run = lambda: psw.slot_mapping(d_qsl, d_pos, d_bt, B, m, out=out)  # noqa: E731
+    warm(torch, run, min_ms=args.warm_ms / 4)
+    ms = timed_events(torch, run, reps=20)
+    alg = n * 12 + need * 4 + (m - n) * 4
     gbs = alg / (ms * 1e-3) / 1e9
+    cast = torch.empty(n, dtype=torch.int32, device="cuda")
+    cp = lambda: cast.copy_(d_pos)  # noqa: E731
+    warm(torch, cp, min_ms=args.warm_ms / 4)
+    ms_copy = timed_events(torch, cp, reps=20)
+    gbs_copy = n * 12 / (ms_copy * 1e-3) / 1e9
     res = {"tokens": n, "max_num_tokens": m, "requests": num_reqs, "block_size": B,
            "ms": round(ms, 5), "algorithmic_bytes": alg, "GBps": round(gbs, 1),
-           "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+           "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "int64_to_int32_copy": {"ms": round(ms_copy, 5), "bytes": n * 12,
+                                   "GBps": round(gbs_copy, 1),
+                                   "frac_of_hbm_peak": round(gbs_copy / HBM_PEAK_GBS, 4)},
+           "frac_of_copy": round(gbs / gbs_copy, 4)}
 
     # the same batch on rank 3 of an 8-rank context-parallel group (interleave 16,
     # 64-token KV blocks): each rank's table holds only its own logical blocks
     world, rank, inter, kvb = 8, 3, 16, 64
+    lens = np.diff(qsl)
     need_cp = -(-lens // (kvb * world)) * (kvb // B)
+    rng = np.random.default_rng(seed + 1)
     bt_cp = np.full((num_reqs, int(need_cp.max())), -1, dtype=np.int32)
     perm = rng.permutation(int(need_cp.sum())).astype(np.int32)
-    off = 0
+    starts = np.concatenate([[0], np.cumsum(need_cp)])
     for r in range(num_reqs):
-        bt_cp[r, :need_cp[r]] = perm[off:off + need_cp[r]]
-        off += need_cp[r]
+        bt_cp[r, :need_cp[r]] = perm[starts[r]:starts[r + 1]]
     d_bt_cp = i32(bt_cp)
 
     def run_cp():
         psw.slot_mapping_cp(d_qsl, d_pos, d_bt_cp, B, m, kv_cache_block_size=kvb,
                             cp_world_size=world, cp_rank=rank, cp_interleave=inter, out=out)
-    warm(torch, run_cp)
-    e0.record()
-    for _ in range(reps):
-        run_cp()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_cp = e0.elapsed_time(e1) / reps
+    warm(torch, run_cp, min_ms=args.warm_ms / 4)
+    ms_cp = timed_events(torch, run_cp, reps=20)
     alg_cp = n * 12 + int(need_cp.sum()) * 4 + (m - n) * 4
     gbs_cp = alg_cp / (ms_cp * 1e-3) / 1e9
     res["context_parallel_rank"] = {
         "cp_world_size": world, "cp_rank": rank, "cp_interleave": inter,
         "kv_cache_block_size": kvb, "ms": round(ms_cp, 5), "algorithmic_bytes": alg_cp,
         "GBps": round(gbs_cp, 1), "frac_of_hbm_peak": round(gbs_cp / HBM_PEAK_GBS, 4)}
+    del d_pos, out, cast
+    torch.cuda.empty_cache()
     return res
 
 
 def bench_decode(args, torch, psw, np):
-    from tests.gpu_setup import bits_to_bf16, i32, i64
+    from tests.gpu_setup import DecodeStep
     from workloads import make_config
-    from workloads.synth import decode_split_ranges
 
     w = make_config(5, decode_splits=args.decode_splits)
     log("decode workload generated")
-    B = w.block_size
+    pdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[args.decode_partials]
+    ds = DecodeStep(w, partial_dtype=pdt)
     R, H, DV = w.num_seqs, w.num_q_heads, w.head_dim_v
-    q = bits_to_bf16(w.q_bits)
-    bt = i32(w.block_table)
-    qsl = i32(w.query_start_loc)
-    seq_lens = i32(w.seq_lens)
-    positions = i64(w.positions)
-    cache = torch.empty((w.num_blocks, B, 1, w.head_dim_qk), dtype=torch.bfloat16, device="cuda")
-    # context rows [0, L-1) go in before timing, through the library itself
-    qsl_ctx = np.concatenate([[0], np.cumsum(w.seq_lens - 1)]).astype(np.int32)
-    pos_ctx = np.concatenate([np.arange(int(L) - 1) for L in w.seq_lens]).astype(np.int64)
-    slots_ctx = psw.slot_mapping(i32(qsl_ctx), i64(pos_ctx), bt, B, int(qsl_ctx[-1]))
-    psw.kv_cache_write(bits_to_bf16(np.concatenate([k[:-1] for k in w.k_bits])), None, slots_ctx,
-                       cache, None)
-    new_rows = bits_to_bf16(np.stack([k[-1] for k in w.k_bits]))
-    del slots_ctx
-    # the history splits and the current key are the key ranges of ONE call: it
-    # emits S + 1 partials (each with its LSE), S history pieces and the current
-    # key's partial last, which lse_combine then merges
-    S = w.key_ranges.shape[0]
-    kr_all = i32(np.concatenate([w.key_ranges, w.current_ranges], axis=0))
-    P = S + 1
-    pdt = torch.float32 if args.decode_partials == "f32" else torch.bfloat16
-    part_o = torch.empty((P, R, H, DV), dtype=pdt, device="cuda")
-    part_l = torch.empty((P, R, H), dtype=torch.float32, device="cuda")
-    out = torch.empty((R * H, DV), dtype=torch.bfloat16, device="cuda")
-    slots = torch.empty(R, dtype=torch.int32, device="cuda")
-    outs = [part_o[j].view(R * H, DV) for j in range(P)]
-    lses = [part_l[j].view(R * H) for j in range(P)]
-    ws_args = psw.ops._attn_args(q, cache, None, bt, qsl, seq_lens, scale=w.scale, window=0,
-                                 causal=True, chunk_size=0, chunk_lookback=-1, mm_ranges=None,
-                                 key_ranges=kr_all, out=part_o, lse=part_l, head_dim_v=DV,
-                                 out_dtype=0, num_splits=P)
-    ws = torch.empty(max(1, psw.ops.attention_workspace_size(ws_args)), dtype=torch.uint8,
-                     device="cuda")
-    # V-up projection of the merged output (128 heads x 512 -> 128 per head)
-    dv_up = 128
-    from workloads.synth import f32_to_bf16_bits
-    w_uv = bits_to_bf16(f32_to_bf16_bits(
-        np.random.default_rng(55).standard_normal((H, DV, dv_up)).astype(np.float32) / DV ** 0.5))
-    vup_out = torch.empty((R, H * dv_up), dtype=torch.bfloat16, device="cuda")
     steps = max(args.steps, 10)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
 
-    def step(i=None):
-        psw.slot_mapping(qsl, positions, bt, B, R, out=slots)
-        psw.kv_cache_write(new_rows, None, slots, cache, None)
-        if i is not None:
-            ev[i][0].record()
-        psw.swa_mm_attention(q, cache, None, bt, qsl, seq_lens, scale=w.scale, window=0,
-                             causal=True, key_ranges=kr_all, head_dim_v=DV, out=part_o,
-                             lse=part_l, out_dtype=pdt, workspace=ws)
-        if i is not None:
-            ev[i][1].record()
-        psw.lse_combine(outs, lses, out=out)
-        if i is not None:
-            ev[i][2].record()
-        psw.vup_projection(out, w_uv, out=vup_out)
-        if i is not None:
-            ev[i][3].record()
-
     def one_call():
-        psw.swa_mm_attention(q, cache, None, bt, qsl, seq_lens, scale=w.scale, window=0,
-                             causal=True, key_ranges=kr_all, head_dim_v=DV, out=part_o,
-                             lse=part_l, out_dtype=pdt, workspace=ws)
-        psw.lse_combine(outs, lses, out=out)
+        ds.attention()
+        ds.combine()
 
     # first, so that the decode kernel's last launches are the timed steps below;
     # one step writes the current keys into the cache
-    step()
-    log("timing decode on two streams")
-    two = bench_two_streams(torch, psw, np, w, q, cache, bt, qsl, seq_lens, kr_all, S, pdt, out,
-                            one_call)
+    ds.run()
+    two = None
+    if not args.skip_extra:
+        log("timing decode on two streams")
+        two = bench_two_streams(args, torch, psw, np, ds, one_call)
     log("timing decode")
     for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+        ds.run()
+    warm_ms = warm(torch, ds.run, min_ms=args.warm_ms)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(steps):
-        step(i)
+        ds.run(ev[i])
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
     attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     comb_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     vup_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
-    vup_bytes = out.numel() * 2 + w_uv.numel() * 2 + vup_out.numel() * 2
+    vup_bytes = ds.out.numel() * 2 + ds.w_uv.numel() * 2 + ds.vup_out.numel() * 2
     kv_bytes = int(w.seq_lens.sum()) * w.head_dim_qk * 2
     # KV rows once + Q + block table + W_UV + the projected output (the merged
     # latent output is an intermediate)
-    alg_bytes = (kv_bytes + q.numel() * 2 + w.block_table.size * 4 + w_uv.numel() * 2
-                 + vup_out.numel() * 2)
+    alg_bytes = (kv_bytes + ds.q.numel() * 2 + w.block_table.size * 4 + ds.w_uv.numel() * 2
+                 + ds.vup_out.numel() * 2)
     gbs = alg_bytes / (ms * 1e-3) / 1e9
-    attn_gbs = (kv_bytes + q.numel() * 2) / (attn_ms * 1e-3) / 1e9
-    return {
+    attn_gbs = (kv_bytes + ds.q.numel() * 2) / (attn_ms * 1e-3) / 1e9
+    res = {
         "workload": "mla_splitkv_decode_b64",
         "unit": "GB/s",
         "value": round(gbs, 1),
@@ -480,30 +572,36 @@ def bench_decode(args, torch, psw, np):
         "algorithmic_bytes_per_step": alg_bytes,
         "attention_ms": round(attn_ms, 5),
         "attention_GBps": round(attn_gbs, 1),
+        "attention_frac_of_hbm_peak": round(attn_gbs / HBM_PEAK_GBS, 4),
         "combine_ms": round(comb_ms, 5),
         "vup_projection": {"ms": round(vup_ms, 5), "algorithmic_bytes": vup_bytes,
                            "GBps": round(vup_bytes / (vup_ms * 1e-3) / 1e9, 1),
-                           "shape": f"[{R}, {H}, {DV}] x [{H}, {DV}, {dv_up}]"},
-        "history_splits": S,
-        "partials": P,
+                           "shape": f"[{R}, {H}, {DV}] x [{H}, {DV}, {ds.dv_up}]"},
+        "history_splits": ds.S,
+        "partials": ds.P,
         "partial_dtype": args.decode_partials,
+        "clock_state": f"steady: {warm_ms:.0f} ms of back-to-back steps before the timed ones",
         "step": "slot_mapping + kv_cache_write + history and current partials (one call) "
                 "+ lse_combine + vup_projection",
-        "two_streams": two,
     }
+    if two is not None:
+        res["two_streams"] = two
+    return res
 
 
-def bench_two_streams(torch, psw, np, w, q, cache, bt, qsl, seq_lens, kr_all, S, pdt, out,
-                      one_call, reps=20, rounds=5):
+def bench_two_streams(args, torch, psw, np, ds, one_call, reps=20, rounds=5):
     """Attention + combine of the decode step four ways: the history splits and
     the current key as ranges of one call; history then current as two calls on
     one stream; history on the main stream and current on a side stream with
     separate workspaces (they may overlap) or one shared workspace (current
     after history), joined before the combine."""
-    DV = w.head_dim_v
-    hist, cur = kr_all[:S].contiguous(), kr_all[S:].contiguous()
+    w = ds.w
+    DV, S = w.head_dim_v, ds.S
+    hist, cur = ds.kr_all[:S].contiguous(), ds.kr_all[S:].contiguous()
     side = torch.cuda.Stream()
     kw = dict(scale=w.scale, window=0, causal=True, head_dim_v=DV)
+    q, cache, bt, qsl, seq_lens, pdt, out = (ds.q, ds.cache, ds.bt, ds.qsl, ds.seq_lens, ds.pdt,
+                                             ds.out)
 
     def two_calls():
         ho, hl = psw.swa_mm_attention(q, cache, None, bt, qsl, seq_lens, key_ranges=hist,
@@ -520,19 +618,6 @@ def bench_two_streams(torch, psw, np, w, q, cache, bt, qsl, seq_lens, kr_all, S,
                                               side_stream=side, partial_dtype=pdt,
                                               shared_workspace=shared, out=out, **kw)
 
-    def timed(fn):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(reps):
-            fn()
-        t1.record()
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / reps
-
     # round-robin rounds, median per variant: the first timings of a run are
     # slower while the clocks settle, which would favour whatever runs last
     variants = {"one_call_ms": one_call, "two_calls_one_stream_ms": two_calls,
@@ -543,7 +628,7 @@ def bench_two_streams(torch, psw, np, w, q, cache, bt, qsl, seq_lens, kr_all, S,
         warm(torch, fn, min_ms=30.0)
     for _ in range(rounds):
         for k, fn in variants.items():
-            times[k].append(timed(fn))
+            times[k].append(timed_events(torch, fn, reps, rounds=1))
     res = {k: round(float(np.median(v)), 5) for k, v in times.items()}
     res["what"] = (f"attention + lse_combine of the decode step, median of {rounds} "
                    f"round-robin rounds of {reps} calls")

@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define PSW_ABI_VERSION 4
+#define PSW_ABI_VERSION 5
 
 enum psw_status {
   PSW_OK = 0,
@@ -44,7 +44,9 @@ enum psw_status {
   PSW_ERR_HIP = -3           /* a HIP launch failed; see psw_last_error() */
 };
 
-enum psw_dtype { PSW_BF16 = 0, PSW_F32 = 1 };
+/* Element types of outputs and partials.  fp16 is IEEE binary16; conversions to
+   bf16 and fp16 round to nearest even. */
+enum psw_dtype { PSW_BF16 = 0, PSW_F32 = 1, PSW_F16 = 2 };
 
 /* Returns PSW_ABI_VERSION. */
 int psw_abi_version(void);
@@ -185,7 +187,9 @@ typedef struct psw_attn_args {
   const int32_t* mm_ranges;       /* int32 [num_seqs, max_mm_ranges, 2] or NULL (no images) */
   const int32_t* key_ranges;      /* int32 [num_splits, num_seqs, 2], or NULL: one split, or
                                      segmented splits when num_splits > 1 (see below) */
-  void* out;                      /* out_dtype [num_splits, num_tokens, num_q_heads, head_dim_v] */
+  void* out;                      /* out_dtype [num_splits, num_tokens, num_q_heads, head_dim_v]:
+                                     the final output, or the split partials in bf16, fp16
+                                     or fp32 (normalised per split; LSE stays fp32) */
   float* lse;                     /* fp32 [num_splits, num_tokens, num_q_heads] or NULL */
   int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v;
   int32_t block_size, block_table_stride, max_mm_ranges;
@@ -193,7 +197,7 @@ typedef struct psw_attn_args {
   int32_t causal;                 /* 1: causal base; 0: bidirectional base */
   int32_t chunk_size, chunk_lookback;  /* chunk_lookback < 0: off */
   int32_t num_splits;             /* >= 1 */
-  int32_t out_dtype;              /* PSW_BF16 or PSW_F32 */
+  int32_t out_dtype;              /* PSW_BF16, PSW_F32 or PSW_F16 */
   float scale;                    /* softmax scale */
   void* workspace;                /* device scratch of >= psw_attention_workspace_size() bytes,
                                      256-byte aligned; may be NULL when that size is 0 */
@@ -250,8 +254,12 @@ int psw_attention_workspace_size(const psw_attn_args* args, int64_t* bytes);
  *     out = sum_p w_p * O_p / sum_p w_p,   out_lse = M + log(sum_p w_p).
  * Partials with lse = -inf weigh 0; a row whose partials are all -inf gets 0 / -inf.
  *   partial_out   host array of P device pointers, each partial_dtype [num_rows, head_dim_v]
+ *                 with partial_dtype PSW_BF16, PSW_F16 or PSW_F32 ([DCP] section 2.1: the
+ *                 history partial reaches the merge in BF16/FP16 without a cast; section
+ *                 3.2: the three history dtypes are all tested)
  *   partial_lse   host array of P device pointers, each fp32 [num_rows]
- *   out           out_dtype [num_rows, head_dim_v] (device); out_lse fp32 [num_rows] or NULL
+ *   out           out_dtype [num_rows, head_dim_v] (device), any of the three types;
+ *                 out_lse fp32 [num_rows] or NULL
  * The partials are read in place (no packing).  1 <= P <= 64; head_dim_v a
  * multiple of 8 and at most 1024.
  */

@@ -18,6 +18,7 @@ PSW_ERR_UNSUPPORTED = -2
 PSW_ERR_HIP = -3
 PSW_BF16 = 0
 PSW_F32 = 1
+PSW_F16 = 2
 
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64

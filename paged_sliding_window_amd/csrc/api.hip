@@ -35,6 +35,9 @@ int check_hip(hipError_t e, const char* what) {
 }
 
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+bool known_dtype(int d) { return d == PSW_BF16 || d == PSW_F32 || d == PSW_F16; }
+static_assert(PSW_BF16 == psw::kOutBf16 && PSW_F32 == psw::kOutF32 && PSW_F16 == psw::kOutF16,
+              "kernel dtype codes are the ABI's");
 int log2i(int v) {
   int l = 0;
   while ((1 << l) < v) ++l;
@@ -179,7 +182,7 @@ static int fill_geometry(const psw_attn_args* a, psw::AttnParams& p, bool need_t
       return fail(PSW_ERR_INVALID, "block_table_stride %d must be >= 1", a->block_table_stride);
     if (a->num_splits < 1)
       return fail(PSW_ERR_INVALID, "num_splits %d must be >= 1", a->num_splits);
-    if (a->out_dtype != PSW_BF16 && a->out_dtype != PSW_F32)
+    if (!known_dtype(a->out_dtype))
       return fail(PSW_ERR_INVALID, "out_dtype %d unknown", a->out_dtype);
     if (!(a->scale > 0.f) || !std::isfinite(a->scale))
       return fail(PSW_ERR_INVALID, "scale must be finite and > 0");
@@ -212,7 +215,7 @@ static int fill_geometry(const psw_attn_args* a, psw::AttnParams& p, bool need_t
   p.geom.chunk_size = a->chunk_size;
   p.geom.chunk_lookback = a->chunk_lookback;
   p.num_splits = a->num_splits;
-  p.out_f32 = a->out_dtype == PSW_F32;
+  p.out_dtype = a->out_dtype;
   p.scale_log2 = a->scale * psw::kLog2eHost;
   return PSW_OK;
 }
@@ -299,9 +302,9 @@ int psw_lse_combine(const void* const* partial_out, const float* const* partial_
   if (num_rows < 0) return fail(PSW_ERR_INVALID, "num_rows < 0");
   if (head_dim_v < 8 || head_dim_v % 8 != 0 || head_dim_v > 1024)
     return fail(PSW_ERR_INVALID, "head_dim_v %d must be a multiple of 8 in [8, 1024]", head_dim_v);
-  if ((partial_dtype != PSW_BF16 && partial_dtype != PSW_F32) ||
-      (out_dtype != PSW_BF16 && out_dtype != PSW_F32))
-    return fail(PSW_ERR_INVALID, "unknown dtype");
+  if (!known_dtype(partial_dtype) || !known_dtype(out_dtype))
+    return fail(PSW_ERR_INVALID, "unknown dtype (partials %d, output %d)", partial_dtype,
+                out_dtype);
   if (partial_out == nullptr || partial_lse == nullptr)
     return fail(PSW_ERR_INVALID, "partial pointer arrays are required");
   psw::CombineArgs parts{};
@@ -312,8 +315,8 @@ int psw_lse_combine(const void* const* partial_out, const float* const* partial_
     parts.lse[i] = partial_lse[i];
   }
   if (num_rows > 0 && out == nullptr) return fail(PSW_ERR_INVALID, "out is NULL");
-  return check_hip(psw::launch_lse_combine(parts, num_partials, partial_dtype == PSW_F32,
-                                           num_rows, head_dim_v, out, out_dtype == PSW_F32,
+  return check_hip(psw::launch_lse_combine(parts, num_partials, partial_dtype, num_rows,
+                                           head_dim_v, out, out_dtype,
                                            out_lse, (hipStream_t)stream),
                    "lse_combine");
 }
@@ -375,7 +378,7 @@ int psw_decode_two_streams(const psw_attn_args* history, const psw_attn_args* cu
     return fail(PSW_ERR_INVALID, "history and current disagree in tokens, query heads or V dim");
   if (history->out_dtype != current->out_dtype)
     return fail(PSW_ERR_INVALID, "history and current partials must share one dtype");
-  if (out_dtype != PSW_BF16 && out_dtype != PSW_F32)
+  if (!known_dtype(out_dtype))
     return fail(PSW_ERR_INVALID, "out_dtype %d unknown", out_dtype);
   const int num_partials = history->num_splits + current->num_splits;
   if (num_partials > psw::kMaxPartials)

@@ -465,25 +465,14 @@ void decode_attention_kernel(const AttnParams p, const DecodeWork wk) {
         // the whole item is in this workgroup's range: final result
         const int64_t orow =
             ((int64_t)d.split * p.num_tokens + d.token) * p.num_q_heads + head0 + hl;
-        if (p.out_f32) {
-          float* dst = static_cast<float*>(p.out) + orow * kDV + dcol;
+        const int64_t e0 = orow * kDV + dcol;
 #pragma unroll
-          for (int b = 0; b < kOBlocks; ++b)
+        for (int b = 0; b < kOBlocks; ++b)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              *reinterpret_cast<float4*>(dst + b * 32 + q * 8) =
-                  make_float4(o[nb][b][4 * q] * inv, o[nb][b][4 * q + 1] * inv,
-                              o[nb][b][4 * q + 2] * inv, o[nb][b][4 * q + 3] * inv);
-        } else {
-          uint16_t* dst = static_cast<uint16_t*>(p.out) + orow * kDV + dcol;
-#pragma unroll
-          for (int b = 0; b < kOBlocks; ++b)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              *reinterpret_cast<bf16x4*>(dst + b * 32 + q * 8) =
-                  to_bf16x4(o[nb][b][4 * q] * inv, o[nb][b][4 * q + 1] * inv,
-                            o[nb][b][4 * q + 2] * inv, o[nb][b][4 * q + 3] * inv);
-        }
+          for (int q = 0; q < 4; ++q)
+            store_out4(p.out, e0 + b * 32 + q * 8, p.out_dtype, o[nb][b][4 * q] * inv,
+                       o[nb][b][4 * q + 1] * inv, o[nb][b][4 * q + 2] * inv,
+                       o[nb][b][4 * q + 3] * inv);
         if (p.lse != nullptr && dh == 0 && half == 0) p.lse[orow] = lse_val;
       } else {
         // a piece of an item shared with neighbouring workgroups
@@ -757,25 +746,18 @@ void decode_full_kernel(const AttnParams p, const DecodeWork wk) {
     // item shared with neighbouring workgroups (fp32, merged later)
     const int64_t orow = ((int64_t)d.split * p.num_tokens + d.token) * p.num_q_heads + head0 + hl;
     const int64_t prow = ((int64_t)group * 2 * G + (p0 < g0 ? 2 * w : 2 * w + 1)) * kHeads + hl;
-    const bool as_bf16 = complete && !p.out_f32;
-    float* dst32 = complete ? static_cast<float*>(p.out) + orow * kDV + dcol
-                            : wk.piece_o + prow * kDV + dcol;
-    uint16_t* dst16 = static_cast<uint16_t*>(p.out) + orow * kDV + dcol;
+    // pieces are fp32; final rows take the caller's output type
+    void* dst = complete ? p.out : static_cast<void*>(wk.piece_o);
+    const int64_t e0 = (complete ? orow : prow) * kDV + dcol;
+    const int odt = complete ? p.out_dtype : kOutF32;
     oacc_settle();
     static_for<kOB>([&](auto bb) {
       constexpr int b = decltype(bb)::value;
       const f32x16 v = oacc_get<b>();
-      if (as_bf16) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<bf16x4*>(dst16 + b * 32 + q * 8) =
-              to_bf16x4(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<float4*>(dst32 + b * 32 + q * 8) =
-              make_float4(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
-      }
+      for (int q = 0; q < 4; ++q)
+        store_out4(dst, e0 + b * 32 + q * 8, odt, v[4 * q] * inv, v[4 * q + 1] * inv,
+                   v[4 * q + 2] * inv, v[4 * q + 3] * inv);
     });
     if (half == 0) {
       if (!complete) wk.piece_lse[prow] = lse_val;
@@ -839,15 +821,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const AttnParams p, c
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  if (p.out_f32) {
-    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow * kDV + lane * 8);
-    dst[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-    dst[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-  } else {
-    *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(p.out) + orow * kDV + lane * 8) =
-        to_bf16x8(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv, acc[4] * inv,
-                  acc[5] * inv, acc[6] * inv, acc[7] * inv);
-  }
+  const int64_t e0 = orow * kDV + lane * 8;
+  store_out4(p.out, e0, p.out_dtype, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  store_out4(p.out, e0 + 4, p.out_dtype, acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
   if (p.lse != nullptr && lane == 0) p.lse[orow] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
 }
 

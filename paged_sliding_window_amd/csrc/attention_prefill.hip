@@ -475,25 +475,13 @@ prefill_attention_kernel(const AttnParams p) {
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (row_valid) {
     const int64_t orow = ((int64_t)split * p.num_tokens + token) * p.num_q_heads + head;
-    if (p.out_f32) {
-      float* dst = static_cast<float*>(p.out) + orow * D + half * 4;
+    const int64_t e0 = orow * D + half * 4;
 #pragma unroll
-      for (int b = 0; b < S::kOBlocks; ++b)
+    for (int b = 0; b < S::kOBlocks; ++b)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<float4*>(dst + b * 32 + g * 8) =
-              make_float4(o[b][4 * g] * inv, o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv,
-                          o[b][4 * g + 3] * inv);
-    } else {
-      uint16_t* dst = static_cast<uint16_t*>(p.out) + orow * D + half * 4;
-#pragma unroll
-      for (int b = 0; b < S::kOBlocks; ++b)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<bf16x4*>(dst + b * 32 + g * 8) =
-              to_bf16x4(o[b][4 * g] * inv, o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv,
-                        o[b][4 * g + 3] * inv);
-    }
+      for (int g = 0; g < 4; ++g)
+        store_out4(p.out, e0 + b * 32 + g * 8, p.out_dtype, o[b][4 * g] * inv,
+                   o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv);
     if (p.lse != nullptr && half == 0)
       p.lse[orow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
   }

@@ -21,6 +21,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Element types of outputs and partials (the psw_dtype values of the C ABI).
+constexpr int kOutBf16 = 0, kOutF32 = 1, kOutF16 = 2;
 
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -91,6 +97,22 @@ __device__ __forceinline__ bf16x4 to_bf16x4(float a0, float a1, float a2, float 
   bf16x2 p0 = __builtin_convertvector((f32x2){a0, a1}, bf16x2);
   bf16x2 p1 = __builtin_convertvector((f32x2){a2, a3}, bf16x2);
   return __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+}
+
+__device__ __forceinline__ f16x4 to_f16x4(float a0, float a1, float a2, float a3) {
+  return f16x4{(_Float16)a0, (_Float16)a1, (_Float16)a2, (_Float16)a3};
+}
+
+// Four consecutive output elements starting at element `elem` of `base`, stored
+// in the output type `dtype` (uniform across the wave).
+__device__ __forceinline__ void store_out4(void* base, int64_t elem, int dtype, float a0, float a1,
+                                           float a2, float a3) {
+  if (dtype == kOutF32)
+    *reinterpret_cast<float4*>(static_cast<float*>(base) + elem) = make_float4(a0, a1, a2, a3);
+  else if (dtype == kOutF16)
+    *reinterpret_cast<f16x4*>(static_cast<_Float16*>(base) + elem) = to_f16x4(a0, a1, a2, a3);
+  else
+    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(base) + elem) = to_bf16x4(a0, a1, a2, a3);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

@@ -7,7 +7,7 @@
 //
 // One wave per row: lane p reads lse_p, the wave reduces max and weight sum,
 // then each lane accumulates eight consecutive output columns over the partials
-// (16-byte loads of bf16, 32-byte loads of fp32 partials).
+// (16-byte loads of bf16 / fp16, 32-byte loads of fp32 partials).
 #include "device_common.h"
 #include "psw_internal.h"
 
@@ -15,7 +15,30 @@ namespace psw {
 
 constexpr int kCombineWaves = 4;
 
-template <bool PART_F32, bool OUT_F32>
+// Eight consecutive elements of a partial, widened to fp32.
+template <int PART>
+__device__ __forceinline__ void load8(const void* base, int64_t elem, float (&v)[8]) {
+  if constexpr (PART == kOutF32) {
+    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+    const float4 a = src[0], b = src[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else if constexpr (PART == kOutF16) {
+    const f16x8 h = *reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(base) + elem);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (float)h[j];
+  } else {
+    const uint4 u4 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+    const uint32_t u[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __builtin_bit_cast(float, u[j] << 16);
+      v[2 * j + 1] = __builtin_bit_cast(float, u[j] & 0xffff0000u);
+    }
+  }
+}
+
+template <int PART, int OUT>
 __global__ __launch_bounds__(kCombineWaves * kWave) void lse_combine_kernel(
     const CombineArgs parts, int num_partials, int64_t num_rows, int head_dim_v,
     void* __restrict__ out, float* __restrict__ out_lse) {
@@ -34,56 +57,49 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void lse_combine_kernel(
       // readlane ignores EXEC: lanes outside this column loop still hold weights
       const float wp = __builtin_bit_cast(
           float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), p));
-      if (PART_F32) {
-        const float4* src =
-            reinterpret_cast<const float4*>(static_cast<const float*>(parts.out[p]) +
-                                            row * head_dim_v + d0);
-        float4 a = src[0], b = src[1];
-        acc[0] += wp * a.x; acc[1] += wp * a.y; acc[2] += wp * a.z; acc[3] += wp * a.w;
-        acc[4] += wp * b.x; acc[5] += wp * b.y; acc[6] += wp * b.z; acc[7] += wp * b.w;
-      } else {
-        const uint4 v = *reinterpret_cast<const uint4*>(
-            static_cast<const uint16_t*>(parts.out[p]) + row * head_dim_v + d0);
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      float v[8];
+      load8<PART>(parts.out[p], row * head_dim_v + d0, v);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[2 * j] += wp * __builtin_bit_cast(float, u[j] << 16);
-          acc[2 * j + 1] += wp * __builtin_bit_cast(float, u[j] & 0xffff0000u);
-        }
-      }
+      for (int j = 0; j < 8; ++j) acc[j] += wp * v[j];
     }
-    if (OUT_F32) {
-      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + row * head_dim_v + d0);
-      dst[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-      dst[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-    } else {
-      bf16x8 o = to_bf16x8(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv,
-                           acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-      *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(out) + row * head_dim_v + d0) = o;
-    }
+    const int64_t e0 = row * head_dim_v + d0;
+    store_out4(out, e0, OUT, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    store_out4(out, e0 + 4, OUT, acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
   }
   if (out_lse != nullptr && lane == 0)
     out_lse[row] = den > 0.f ? M + __logf(den) : -INFINITY;
 }
 
-hipError_t launch_lse_combine(const CombineArgs& parts, int num_partials, int partial_f32,
-                              int64_t num_rows, int head_dim_v, void* out, int out_f32,
+template <int PART>
+static void launch_combine_out(const CombineArgs& parts, int num_partials, int64_t num_rows,
+                               int head_dim_v, void* out, int out_dtype, float* out_lse,
+                               dim3 grid, dim3 block, hipStream_t stream) {
+  if (out_dtype == kOutF32)
+    hipLaunchKernelGGL((lse_combine_kernel<PART, kOutF32>), grid, block, 0, stream, parts,
+                       num_partials, num_rows, head_dim_v, out, out_lse);
+  else if (out_dtype == kOutF16)
+    hipLaunchKernelGGL((lse_combine_kernel<PART, kOutF16>), grid, block, 0, stream, parts,
+                       num_partials, num_rows, head_dim_v, out, out_lse);
+  else
+    hipLaunchKernelGGL((lse_combine_kernel<PART, kOutBf16>), grid, block, 0, stream, parts,
+                       num_partials, num_rows, head_dim_v, out, out_lse);
+}
+
+hipError_t launch_lse_combine(const CombineArgs& parts, int num_partials, int partial_dtype,
+                              int64_t num_rows, int head_dim_v, void* out, int out_dtype,
                               float* out_lse, hipStream_t stream) {
   if (num_rows == 0) return hipSuccess;
   const dim3 grid((unsigned)((num_rows + kCombineWaves - 1) / kCombineWaves));
   const dim3 block(kCombineWaves * kWave);
-  if (partial_f32 && out_f32)
-    hipLaunchKernelGGL((lse_combine_kernel<true, true>), grid, block, 0, stream, parts,
-                       num_partials, num_rows, head_dim_v, out, out_lse);
-  else if (partial_f32)
-    hipLaunchKernelGGL((lse_combine_kernel<true, false>), grid, block, 0, stream, parts,
-                       num_partials, num_rows, head_dim_v, out, out_lse);
-  else if (out_f32)
-    hipLaunchKernelGGL((lse_combine_kernel<false, true>), grid, block, 0, stream, parts,
-                       num_partials, num_rows, head_dim_v, out, out_lse);
+  if (partial_dtype == kOutF32)
+    launch_combine_out<kOutF32>(parts, num_partials, num_rows, head_dim_v, out, out_dtype,
+                                out_lse, grid, block, stream);
+  else if (partial_dtype == kOutF16)
+    launch_combine_out<kOutF16>(parts, num_partials, num_rows, head_dim_v, out, out_dtype,
+                                out_lse, grid, block, stream);
   else
-    hipLaunchKernelGGL((lse_combine_kernel<false, false>), grid, block, 0, stream, parts,
-                       num_partials, num_rows, head_dim_v, out, out_lse);
+    launch_combine_out<kOutBf16>(parts, num_partials, num_rows, head_dim_v, out, out_dtype,
+                                 out_lse, grid, block, stream);
   return hipGetLastError();
 }
 

@@ -23,7 +23,8 @@ struct AttnParams {
   int head_dim_qk, head_dim_v;
   int block_size_log2, block_table_stride, max_mm_ranges;
   MaskGeom geom;
-  int num_splits, out_f32;
+  int num_splits;
+  int out_dtype;  // kOutBf16, kOutF32 or kOutF16 (the psw_dtype values)
   float scale_log2;  // softmax scale * log2(e)
 };
 
@@ -49,8 +50,8 @@ struct CombineArgs {
   const void* out[kMaxPartials];
   const float* lse[kMaxPartials];
 };
-hipError_t launch_lse_combine(const CombineArgs& parts, int num_partials, int partial_f32,
-                              int64_t num_rows, int head_dim_v, void* out, int out_f32,
+hipError_t launch_lse_combine(const CombineArgs& parts, int num_partials, int partial_dtype,
+                              int64_t num_rows, int head_dim_v, void* out, int out_dtype,
                               float* out_lse, hipStream_t stream);
 
 // V-up projection: out[t, h, :] = x[t, h, :] @ w[h] (bf16 in and out, fp32 accumulation).

@@ -7,7 +7,84 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import PSW_BF16, PSW_F32, PswAttnArgs, check, load
+from ._lib import PSW_BF16, PSW_F16, PSW_F32, PswAttnArgs, check, load
+
+# torch element types of outputs and partials -> psw_dtype codes
+_DTYPES = {torch.bfloat16: PSW_BF16, torch.float32: PSW_F32, torch.float16: PSW_F16}
+
+
+def _dtype_code(dt: torch.dtype, what: str) -> int:
+    if dt not in _DTYPES:
+        raise TypeError(f"{what} must be bfloat16, float16 or float32, got {dt}")
+    return _DTYPES[dt]
+
+
+# ---- shape consistency (host only; raise before anything is enqueued) -------
+
+def check_kv_write_shapes(k_new, v_new, slots_numel, k_cache, v_cache) -> None:
+    """k_new [N, Hkv, Dk] and v_new [N, Hkv, Dv] (or None) against the caches
+    [num_blocks, B, Hkv, Dk] / [num_blocks, B, Hkv, Dv]; arguments are shapes."""
+    k_new, k_cache = tuple(k_new), tuple(k_cache)
+    if len(k_new) != 3 or len(k_cache) != 4:
+        raise ValueError(f"k_new {k_new} must be 3-D and k_cache {k_cache} 4-D")
+    if k_cache[2:] != k_new[1:]:
+        raise ValueError(f"k_cache heads/dim {k_cache[2:]} differ from k_new's {k_new[1:]}")
+    if (v_new is None) != (v_cache is None):
+        raise ValueError("v_new and v_cache must both be given or both be None")
+    if v_new is not None:
+        v_new, v_cache = tuple(v_new), tuple(v_cache)
+        if len(v_new) != 3 or len(v_cache) != 4:
+            raise ValueError(f"v_new {v_new} must be 3-D and v_cache {v_cache} 4-D")
+        if v_new[:2] != k_new[:2]:
+            raise ValueError(f"v_new rows/heads {v_new[:2]} differ from k_new's {k_new[:2]}")
+        if v_cache[2:] != v_new[1:]:
+            raise ValueError(f"v_cache heads/dim {v_cache[2:]} differ from v_new's {v_new[1:]}")
+        if v_cache[:2] != k_cache[:2]:
+            raise ValueError(f"v_cache blocks {v_cache[:2]} differ from k_cache's {k_cache[:2]}")
+    if slots_numel < k_new[0]:
+        raise ValueError("slot_mapping shorter than the new rows")
+
+
+def check_attention_shapes(q, k_cache, v_cache, block_table, qsl_numel, seq_lens_numel,
+                           mm_ranges, key_ranges, head_dim_v) -> None:
+    """Shapes of one attention call (tuples; v_cache, mm_ranges, key_ranges may
+    be None): every extent the kernels index with must agree."""
+    q, k_cache, block_table = tuple(q), tuple(k_cache), tuple(block_table)
+    num_seqs = qsl_numel - 1
+    if num_seqs < 0:
+        raise ValueError("query_start_loc needs num_seqs + 1 >= 1 entries")
+    if len(q) != 3 or len(k_cache) != 4 or len(block_table) != 2:
+        raise ValueError("q must be 3-D, k_cache 4-D and block_table 2-D")
+    if k_cache[3] != q[2]:
+        raise ValueError(f"k_cache head dim {k_cache[3]} differs from q's {q[2]}")
+    if k_cache[2] < 1 or q[1] % k_cache[2] != 0:
+        raise ValueError(f"{q[1]} query heads are not a multiple of {k_cache[2]} KV heads")
+    if v_cache is not None:
+        v_cache = tuple(v_cache)
+        if len(v_cache) != 4 or v_cache[:3] != k_cache[:3]:
+            raise ValueError(f"v_cache {v_cache} does not match k_cache {k_cache} in blocks, "
+                             "block size and heads")
+    elif head_dim_v is None or not (0 < head_dim_v <= k_cache[3]):
+        raise ValueError("a latent cache (v_cache None) needs 0 < head_dim_v <= its row width")
+    if seq_lens_numel != num_seqs:
+        raise ValueError(f"seq_lens has {seq_lens_numel} entries for {num_seqs} sequences")
+    if block_table[0] < num_seqs:
+        raise ValueError(f"block_table has {block_table[0]} rows for {num_seqs} sequences")
+    if mm_ranges is not None:
+        mm_ranges = tuple(mm_ranges)
+        if len(mm_ranges) != 3 or mm_ranges[0] != num_seqs or mm_ranges[2] != 2:
+            raise ValueError(f"mm_ranges {mm_ranges} must be [num_seqs={num_seqs}, max, 2]")
+    if key_ranges is not None:
+        key_ranges = tuple(key_ranges)
+        if len(key_ranges) != 3 or key_ranges[1:] != (num_seqs, 2):
+            raise ValueError(f"key_ranges {key_ranges} must be [splits, num_seqs={num_seqs}, 2]")
+
+
+def check_combine_shapes(rows, dv, out_numel, out_lse_numel) -> None:
+    if out_numel != rows * dv:
+        raise ValueError(f"out holds {out_numel} elements, the merge writes {rows} x {dv}")
+    if out_lse_numel is not None and out_lse_numel != rows:
+        raise ValueError(f"out_lse holds {out_lse_numel} elements for {rows} rows")
 
 
 def _stream(stream=None) -> int:
@@ -38,6 +115,8 @@ def slot_mapping(query_start_loc: torch.Tensor, positions: torch.Tensor, block_t
     _need(query_start_loc, "query_start_loc", torch.int32, 1)
     _need(positions, "positions", torch.int64, 1)
     _need(block_table, "block_table", torch.int32, 2)
+    if block_table.shape[0] < query_start_loc.numel() - 1:
+        raise ValueError("block_table has fewer rows than requests")
     if out is None:
         out = torch.empty(max_num_tokens, dtype=torch.int32, device=positions.device)
     _need(out, "out", torch.int32, 1)
@@ -60,6 +139,8 @@ def slot_mapping_cp(query_start_loc: torch.Tensor, positions: torch.Tensor,
     _need(query_start_loc, "query_start_loc", torch.int32, 1)
     _need(positions, "positions", torch.int64, 1)
     _need(block_table, "block_table", torch.int32, 2)
+    if block_table.shape[0] < query_start_loc.numel() - 1:
+        raise ValueError("block_table has fewer rows than requests")
     if out is None:
         out = torch.empty(max_num_tokens, dtype=torch.int32, device=positions.device)
     _need(out, "out", torch.int32, 1)
@@ -85,10 +166,11 @@ def kv_cache_write(k_new: torch.Tensor, v_new: Optional[torch.Tensor], slots: to
     dv = 0
     if v_new is not None:
         _need(v_new, "v_new", torch.bfloat16, 3)
-        _need(v_cache, "v_cache", torch.bfloat16, 4)
         dv = v_new.shape[2]
-    if slots.numel() < n:
-        raise ValueError("slot_mapping shorter than the new rows")
+    if v_cache is not None:
+        _need(v_cache, "v_cache", torch.bfloat16, 4)
+    check_kv_write_shapes(k_new.shape, None if v_new is None else v_new.shape, slots.numel(),
+                          k_cache.shape, None if v_cache is None else v_cache.shape)
     num_slots = k_cache.shape[0] * k_cache.shape[1]
     check(load().psw_kv_cache_write(_ptr(k_new), _ptr(v_new), _ptr(slots), n, hkv, dk, dv,
                                     _ptr(k_cache), _ptr(v_cache), num_slots, _stream(stream)))
@@ -147,8 +229,12 @@ def _prepare_attention(q, k_cache, v_cache, block_table, query_start_loc, seq_le
         num_splits = key_ranges.shape[0]
     elif num_splits is None:
         num_splits = 1
+    check_attention_shapes(q.shape, k_cache.shape, None if v_cache is None else v_cache.shape,
+                           block_table.shape, query_start_loc.numel(), seq_lens.numel(),
+                           None if mm_ranges is None else mm_ranges.shape,
+                           None if key_ranges is None else key_ranges.shape, head_dim_v)
     n, hq = q.shape[0], q.shape[1]
-    odt = {torch.bfloat16: PSW_BF16, torch.float32: PSW_F32}[out_dtype]
+    odt = _dtype_code(out_dtype, "out_dtype")
     if out is None:
         out = torch.empty((num_splits, n, hq, head_dim_v), dtype=out_dtype, device=q.device)
     _need(out, "out", out_dtype)
@@ -264,7 +350,7 @@ def decode_two_streams(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional
               cw):
         if t is not None:
             t.record_stream(side_stream)
-    odt = {torch.bfloat16: PSW_BF16, torch.float32: PSW_F32}[out_dtype]
+    odt = _dtype_code(out_dtype, "out_dtype")
     check(load().psw_decode_two_streams(ctypes.byref(ah), ctypes.byref(ac), _ptr(out), odt,
                                         _ptr(out_lse), main.cuda_stream, side_stream.cuda_stream))
     return out, out_lse, (ho, hl), (co, cl)
@@ -280,7 +366,7 @@ def attention_workspace_size(args: PswAttnArgs) -> int:
 def lse_combine(partial_outs: Sequence[torch.Tensor], partial_lses: Sequence[torch.Tensor],
                 out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
                 out_dtype: torch.dtype = torch.bfloat16, stream=None):
-    """Merge P partials [rows, Dv] (fp32 or bf16) with lse [rows] fp32 in place."""
+    """Merge P partials [rows, Dv] (bf16, fp16 or fp32) with lse [rows] fp32, read in place."""
     P = len(partial_outs)
     if P != len(partial_lses) or P == 0:
         raise ValueError("need as many LSE tensors as partial outputs, at least one")
@@ -298,12 +384,12 @@ def lse_combine(partial_outs: Sequence[torch.Tensor], partial_lses: Sequence[tor
     _need(out, "out", out_dtype)
     if out_lse is not None:
         _need(out_lse, "out_lse", torch.float32)
+    check_combine_shapes(rows, dv, out.numel(), None if out_lse is None else out_lse.numel())
     po = (ctypes.c_void_p * P)(*[o.data_ptr() for o in partial_outs])
     pl = (ctypes.c_void_p * P)(*[l.data_ptr() for l in partial_lses])
-    check(load().psw_lse_combine(po, pl, P, {torch.bfloat16: PSW_BF16, torch.float32: PSW_F32}[pdt],
-                                 rows, dv, _ptr(out),
-                                 {torch.bfloat16: PSW_BF16, torch.float32: PSW_F32}[out_dtype],
-                                 _ptr(out_lse), _stream(stream)))
+    check(load().psw_lse_combine(po, pl, P, _dtype_code(pdt, "partial dtype"), rows, dv,
+                                 _ptr(out), _dtype_code(out_dtype, "out_dtype"), _ptr(out_lse),
+                                 _stream(stream)))
     return out if out_lse is None else (out, out_lse)
 
 
@@ -350,6 +436,8 @@ def tile_bounds(query_start_loc: torch.Tensor, seq_lens: torch.Tensor,
     a.window, a.causal = int(window), int(bool(causal))
     a.chunk_size, a.chunk_lookback = int(chunk_size), int(chunk_lookback)
     n = seq_idx.numel()
+    if q_block_idx.numel() != n:
+        raise ValueError("seq_idx and q_block_idx must have the same length")
     out = torch.empty((n, 3), dtype=torch.int32, device=seq_idx.device)
     check(load().psw_tile_bounds(ctypes.byref(a), int(tile_size), int(block_m), int(block_q),
                                  _ptr(seq_idx), _ptr(q_block_idx), n, _ptr(out), _stream(stream)))

@@ -98,3 +98,88 @@ def assert_lse_close(got, ref, what=""):
     assert np.array_equal(np.isneginf(got), np.isneginf(ref)), f"{what}: -inf pattern differs"
     fin = np.isfinite(ref)
     assert_close(got[fin], ref[fin], what)
+
+
+class DecodeStep:
+    """The latent decode step as bench.py times it, on the GPU: context rows
+    [0, L-1) are written to the paged latent cache beforehand through the
+    library's slot mapping and KV write; one step is then
+      slot mapping of the new token -> latent KV write -> ONE attention call
+      whose key ranges are the history splits followed by the current key
+      (S + 1 partials, each with its LSE) -> LSE combine -> V-up projection.
+    """
+
+    def __init__(self, w, partial_dtype=torch.bfloat16, dv_up=128, wuv_seed=55):
+        from workloads.synth import f32_to_bf16_bits
+        self.w = w
+        B = w.block_size
+        R, H, DV = w.num_seqs, w.num_q_heads, w.head_dim_v
+        self.q = bits_to_bf16(w.q_bits)
+        self.bt = i32(w.block_table)
+        self.qsl = i32(w.query_start_loc)
+        self.seq_lens = i32(w.seq_lens)
+        self.positions = i64(w.positions)
+        self.cache = torch.empty((w.num_blocks, B, 1, w.head_dim_qk), dtype=torch.bfloat16,
+                                 device="cuda")
+        qsl_ctx = np.concatenate([[0], np.cumsum(w.seq_lens - 1)]).astype(np.int32)
+        pos_ctx = np.concatenate([np.arange(int(L) - 1) for L in w.seq_lens]).astype(np.int64)
+        slots_ctx = psw.slot_mapping(i32(qsl_ctx), i64(pos_ctx), self.bt, B, int(qsl_ctx[-1]))
+        psw.kv_cache_write(bits_to_bf16(np.concatenate([k[:-1] for k in w.k_bits])), None,
+                           slots_ctx, self.cache, None)
+        del slots_ctx
+        self.new_rows = bits_to_bf16(np.stack([k[-1] for k in w.k_bits]))
+        self.S = w.key_ranges.shape[0]
+        self.P = self.S + 1
+        self.kr_all = i32(np.concatenate([w.key_ranges, w.current_ranges], axis=0))
+        self.pdt = partial_dtype
+        self.part_o = torch.empty((self.P, R, H, DV), dtype=partial_dtype, device="cuda")
+        self.part_l = torch.empty((self.P, R, H), dtype=torch.float32, device="cuda")
+        self.out = torch.empty((R * H, DV), dtype=torch.bfloat16, device="cuda")
+        self.out_lse = torch.empty(R * H, dtype=torch.float32, device="cuda")
+        self.slots = torch.empty(R, dtype=torch.int32, device="cuda")
+        self.outs = [self.part_o[j].view(R * H, DV) for j in range(self.P)]
+        self.lses = [self.part_l[j].view(R * H) for j in range(self.P)]
+        args = psw.ops._attn_args(self.q, self.cache, None, self.bt, self.qsl, self.seq_lens,
+                                  scale=w.scale, window=0, causal=True, chunk_size=0,
+                                  chunk_lookback=-1, mm_ranges=None, key_ranges=self.kr_all,
+                                  out=self.part_o, lse=self.part_l, head_dim_v=DV, out_dtype=0,
+                                  num_splits=self.P)
+        self.ws = torch.empty(max(1, psw.ops.attention_workspace_size(args)), dtype=torch.uint8,
+                              device="cuda")
+        self.dv_up = dv_up
+        self.wuv_f32 = (np.random.default_rng(wuv_seed).standard_normal((H, DV, dv_up))
+                        .astype(np.float32) / DV ** 0.5)
+        wuv_bits = f32_to_bf16_bits(self.wuv_f32)
+        self.w_uv = bits_to_bf16(wuv_bits)
+        from workloads.synth import bf16_bits_to_f32
+        self.wuv_f32 = bf16_bits_to_f32(wuv_bits)   # the values the kernel reads
+        self.vup_out = torch.empty((R, H * dv_up), dtype=torch.bfloat16, device="cuda")
+
+    def attention(self):
+        w = self.w
+        psw.swa_mm_attention(self.q, self.cache, None, self.bt, self.qsl, self.seq_lens,
+                             scale=w.scale, window=0, causal=True, key_ranges=self.kr_all,
+                             head_dim_v=w.head_dim_v, out=self.part_o, lse=self.part_l,
+                             out_dtype=self.pdt, workspace=self.ws)
+
+    def combine(self):
+        psw.lse_combine(self.outs, self.lses, out=self.out, out_lse=self.out_lse)
+
+    def run(self, ev=None):
+        """One step; ev = 4 events recorded before the attention, after it, after
+        the combine and after the projection (or None)."""
+        w = self.w
+        psw.slot_mapping(self.qsl, self.positions, self.bt, w.block_size, w.num_seqs,
+                         out=self.slots)
+        psw.kv_cache_write(self.new_rows, None, self.slots, self.cache, None)
+        if ev is not None:
+            ev[0].record()
+        self.attention()
+        if ev is not None:
+            ev[1].record()
+        self.combine()
+        if ev is not None:
+            ev[2].record()
+        psw.vup_projection(self.out, self.w_uv, out=self.vup_out)
+        if ev is not None:
+            ev[3].record()

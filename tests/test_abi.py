@@ -10,6 +10,20 @@ import pytest
 import paged_sliding_window_amd as psw
 from paged_sliding_window_amd._lib import (EXPORTS, PSW_ERR_INVALID, PSW_ERR_UNSUPPORTED, PSW_OK,
                                             PswAttnArgs)
+from paged_sliding_window_amd.ops import (check_attention_shapes, check_combine_shapes,
+                                          check_kv_write_shapes)
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.is_available()
+
+
+# Cases that hand the library made-up device addresses rely on its host-side
+# checks failing first.  Where a GPU is visible a regression in those checks
+# would launch a kernel on such an address, so they run only without one.
+no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="made-up device addresses: host-only "
+                                 "check, skipped where a GPU is visible")
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "psw.h")
 
@@ -32,7 +46,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     lib = psw.load()
-    assert lib.psw_abi_version() == 4
+    assert lib.psw_abi_version() == 5
     assert lib.psw_status_string(PSW_OK) == b"ok"
     assert lib.psw_status_string(PSW_ERR_INVALID) == b"invalid argument"
 
@@ -112,6 +126,7 @@ def test_workspace_size_query():
     assert lib.psw_attention_workspace_size(ctypes.byref(_args()), None) == PSW_ERR_INVALID
 
 
+@no_gpu_only
 def test_latent_decode_rejects_missing_or_small_workspace():
     lib = psw.load()
     fake = 0x100000  # never dereferenced: the call fails on the host
@@ -128,6 +143,7 @@ def test_latent_decode_rejects_missing_or_small_workspace():
     assert lib.psw_swa_mm_attention(ctypes.byref(misaligned), None) == PSW_ERR_INVALID
 
 
+@no_gpu_only
 def test_two_stream_decode_checks_both_calls_before_enqueuing():
     # every failure below is found on the host; no pointer is dereferenced
     lib = psw.load()
@@ -166,3 +182,77 @@ def test_two_stream_decode_checks_both_calls_before_enqueuing():
     # an empty batch has nothing to enqueue
     empty = _args()
     assert call(empty, empty) == PSW_OK
+
+
+def test_fp16_is_a_known_dtype():
+    lib = psw.load()
+    assert lib.psw_swa_mm_attention(ctypes.byref(_args(out_dtype=2)), None) == PSW_OK
+    assert lib.psw_swa_mm_attention(ctypes.byref(_args(out_dtype=3)), None) == PSW_ERR_INVALID
+    po = (ctypes.c_void_p * 1)()
+    # no rows: accepted for every partial / output type pair, nothing launched
+    for pd in (0, 1, 2):
+        for od in (0, 1, 2):
+            assert lib.psw_lse_combine(po, po, 1, pd, 0, 64, None, od, None, None) == PSW_OK
+    assert lib.psw_lse_combine(po, po, 1, 3, 0, 64, None, 0, None, None) == PSW_ERR_INVALID
+
+
+# ---- wrapper shape checks (host logic of ops.py; shapes only) ---------------
+
+ATTN_OK = dict(q=(10, 8, 128), k_cache=(20, 16, 2, 128), v_cache=(20, 16, 2, 128),
+               block_table=(3, 7), qsl_numel=4, seq_lens_numel=3, mm_ranges=(3, 2, 2),
+               key_ranges=None, head_dim_v=None)
+
+
+def test_attention_shapes_accepted():
+    check_attention_shapes(**ATTN_OK)
+    check_attention_shapes(**dict(ATTN_OK, key_ranges=(2, 3, 2), mm_ranges=None))
+    # latent cache: V is the first head_dim_v columns of K
+    check_attention_shapes(**dict(ATTN_OK, q=(4, 128, 576), k_cache=(9, 64, 1, 576),
+                                  v_cache=None, head_dim_v=512))
+
+
+@pytest.mark.parametrize("change", [
+    dict(q=(10, 8, 64)),                       # q head dim != cache head dim
+    dict(q=(10, 7, 128)),                      # query heads not a multiple of KV heads
+    dict(v_cache=(20, 16, 1, 128)),            # V heads differ from K heads
+    dict(v_cache=(21, 16, 2, 128)),            # V blocks differ from K blocks
+    dict(seq_lens_numel=2),                    # seq_lens shorter than num_seqs
+    dict(block_table=(2, 7)),                  # fewer table rows than sequences
+    dict(mm_ranges=(2, 2, 2)),                 # ranges for the wrong number of sequences
+    dict(mm_ranges=(3, 2, 3)),                 # ranges not (start, end) pairs
+    dict(key_ranges=(2, 4, 2)),                # key ranges for the wrong number of sequences
+    dict(key_ranges=(2, 3)),                   # key ranges not 3-D
+    dict(v_cache=None, head_dim_v=None),       # latent cache without head_dim_v
+    dict(v_cache=None, head_dim_v=129),        # latent V wider than the row
+    dict(qsl_numel=0),                         # no query_start_loc entries
+], ids=lambda d: ",".join(d))
+def test_attention_shape_mismatches_raise(change):
+    with pytest.raises(ValueError):
+        check_attention_shapes(**dict(ATTN_OK, **change))
+
+
+def test_kv_write_shapes():
+    check_kv_write_shapes((5, 2, 64), (5, 2, 32), 5, (9, 16, 2, 64), (9, 16, 2, 32))
+    check_kv_write_shapes((5, 1, 576), None, 8, (9, 64, 1, 576), None)
+    bad = [
+        ((5, 2, 64), (5, 2, 32), 5, (9, 16, 1, 64), (9, 16, 2, 32)),   # K heads
+        ((5, 2, 64), (5, 2, 32), 5, (9, 16, 2, 32), (9, 16, 2, 32)),   # K dim
+        ((5, 2, 64), (4, 2, 32), 5, (9, 16, 2, 64), (9, 16, 2, 32)),   # V rows
+        ((5, 2, 64), (5, 1, 32), 5, (9, 16, 2, 64), (9, 16, 2, 32)),   # V heads
+        ((5, 2, 64), (5, 2, 32), 5, (9, 16, 2, 64), (9, 16, 2, 16)),   # V dim
+        ((5, 2, 64), (5, 2, 32), 5, (9, 16, 2, 64), (8, 16, 2, 32)),   # V blocks
+        ((5, 2, 64), (5, 2, 32), 4, (9, 16, 2, 64), (9, 16, 2, 32)),   # slots too short
+        ((5, 2, 64), None, 5, (9, 16, 2, 64), (9, 16, 2, 32)),         # V cache without V
+    ]
+    for args in bad:
+        with pytest.raises(ValueError):
+            check_kv_write_shapes(*args)
+
+
+def test_combine_shapes():
+    check_combine_shapes(10, 64, 640, 10)
+    check_combine_shapes(10, 64, 640, None)
+    with pytest.raises(ValueError):
+        check_combine_shapes(10, 64, 639, None)
+    with pytest.raises(ValueError):
+        check_combine_shapes(10, 64, 640, 9)

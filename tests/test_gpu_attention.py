@@ -48,24 +48,19 @@ def test_batched_chunked_prefill_full():
     _check(gw, out, lse)
 
 
-def test_noncausal_chunk_lookback_sampled():
+def test_noncausal_chunk_lookback_full():
+    """The non-causal chunk-lookback workload, every row of both requests."""
     gw = GpuWorkload(make_config(4))
     out, lse = gw.attention()
-    _check(gw, out, lse, rows_per_seq=600, seed=4)
+    _check(gw, out, lse)
 
 
-def test_gemma_multimodal_prefill_full_size_sampled():
+def test_gemma_multimodal_prefill_full_size():
+    """The 16,550-token multimodal workload: every row, every head, out and LSE."""
     w = make_config(2)
     gw = GpuWorkload(w)
     out, lse = gw.attention()
-    # rows around every image boundary plus random rows
-    rows = set(np.random.default_rng(2).choice(16550, 200, replace=False).tolist())
-    for s, e in w.ranges_of(0)[::6]:
-        rows.update([s - 1, s, s + 1, e - 1, e, e + 1])
-    rows = np.array(sorted(x for x in rows if 0 <= x < 16550))
-    ref_o, ref_l = oracle_rows(w, 0, rows)
-    assert_close(out.float().cpu().numpy()[rows], ref_o, "gemma out")
-    assert_lse_close(lse.cpu().numpy()[rows], ref_l, "gemma lse")
+    _check(gw, out, lse)
 
 
 @pytest.mark.parametrize("seed", range(16))
@@ -81,8 +76,9 @@ def test_random_small_cases(seed):
     _check(gw, out, lse)
 
 
-@pytest.mark.parametrize("seed", range(4))
-def test_key_split_partials_and_fp32_output(seed):
+@pytest.mark.parametrize("seed,pdt", [(0, torch.float32), (1, torch.float32), (2, torch.float16),
+                                      (3, torch.bfloat16)])
+def test_key_split_partials(seed, pdt):
     w = make_small_case(700 + seed, num_seqs=3, max_len=500, hq=4, hkv=2, d=128)
     gw = GpuWorkload(w)
     rng = np.random.default_rng(seed)
@@ -93,8 +89,8 @@ def test_key_split_partials_and_fp32_output(seed):
         cuts = np.sort(rng.integers(0, L + 1, size=S - 1))
         edges = np.concatenate([[0], cuts, [L]])
         kr[:, r, 0], kr[:, r, 1] = edges[:-1], edges[1:]
-    out, lse = gw.attention(key_ranges=kr, out_dtype=torch.float32)
-    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    out, lse = gw.attention(key_ranges=kr, out_dtype=pdt)
+    out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
     for j in range(S):
         for r in range(w.num_seqs):
             s0, s1 = int(w.query_start_loc[r]), int(w.query_start_loc[r + 1])

@@ -6,10 +6,58 @@ import torch
 
 import paged_sliding_window_amd as psw
 from oracle import lse_merge_ref
-from tests.gpu_setup import (GpuWorkload, assert_close, assert_lse_close, i32, oracle_rows)
+from tests.gpu_setup import (DecodeStep, GpuWorkload, assert_close, assert_lse_close, i32,
+                             oracle_rows)
 from workloads import make_config, make_small_case
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bench_decode_oracle():
+    """Oracle of the decode workload as the bench runs it (history as one split
+    [0, L-1), the current key [L-1, L)): per request the merged row, the
+    history partial and the current partial, all 128 heads."""
+    w = make_config(5, decode_splits=1)
+    full, hist, cur = [], [], []
+    for r in range(w.num_seqs):
+        full.append(oracle_rows(w, r))
+        hist.append(oracle_rows(w, r, key_range=tuple(w.key_ranges[0, r])))
+        cur.append(oracle_rows(w, r, key_range=tuple(w.current_ranges[0, r])))
+    return w, full, hist, cur
+
+
+@pytest.mark.parametrize("pdt", [torch.bfloat16, torch.float16, torch.float32],
+                         ids=["bf16", "f16", "f32"])
+def test_bench_decode_step_full_size(bench_decode_oracle, pdt):
+    """Exactly the decode step bench.py times (64 requests x 128 heads, one
+    attention call over [history, current] key ranges, partials in pdt, LSE
+    combine, V-up projection), run twice: every element of both partials and
+    their LSEs, the merged output and LSE, and the projected output against the
+    oracle ([DCP] stage 3 sections 3.1-3.2 and code blocks B-D; "Terms" and
+    block A for the projection)."""
+    from oracle import vup_projection_ref
+    w, full, hist, cur = bench_decode_oracle
+    ds = DecodeStep(w, partial_dtype=pdt)
+    ds.run()
+    ds.run()   # the step again on its own outputs: the cache write is idempotent
+    torch.cuda.synchronize()
+    R, H, DV = w.num_seqs, w.num_q_heads, w.head_dim_v
+    po = ds.part_o.float().cpu().numpy()
+    pl = ds.part_l.cpu().numpy()
+    out = ds.out.float().cpu().numpy().reshape(R, H, DV)
+    lse = ds.out_lse.cpu().numpy().reshape(R, H)
+    merged_ref = np.zeros((R, H, DV))
+    for r in range(R):
+        assert_close(po[0, r], hist[r][0][0], f"history partial of {r}")
+        assert_lse_close(pl[0, r], hist[r][1][0], f"history lse of {r}")
+        assert_close(po[1, r], cur[r][0][0], f"current partial of {r}")
+        assert_lse_close(pl[1, r], cur[r][1][0], f"current lse of {r}")
+        assert_close(out[r], full[r][0][0], f"merged row of {r}")
+        assert_lse_close(lse[r], full[r][1][0], f"merged lse of {r}")
+        merged_ref[r] = full[r][0][0]
+    proj = ds.vup_out.float().cpu().numpy().reshape(R, H, ds.dv_up)
+    assert_close(proj, vup_projection_ref(merged_ref, ds.wuv_f32), "projected output")
 
 
 def _decode(gw, w, partial_dtype=torch.float32):
@@ -45,12 +93,13 @@ def test_mla_decode_full_size():
         assert_close(cur_o[0, r].cpu().numpy(), ref_o[0], f"current of {r}")
 
 
-@pytest.mark.parametrize("seed", range(4))
-def test_small_latent_decode_bf16_partials(seed):
+@pytest.mark.parametrize("seed,pdt", [(0, torch.bfloat16), (1, torch.bfloat16), (2, torch.float16),
+                                      (3, torch.float16)])
+def test_small_latent_decode_half_partials(seed, pdt):
     # one new token per request: the last position of each request
     w = _small_decode_case(900 + seed)
     gw = GpuWorkload(w)
-    out, lse, *_ = _decode(gw, w, partial_dtype=torch.bfloat16)
+    out, lse, *_ = _decode(gw, w, partial_dtype=pdt)
     out = out.float().cpu().numpy().reshape(w.num_tokens, w.num_q_heads, w.head_dim_v)
     for r in range(w.num_seqs):
         ref_o, _ = oracle_rows(w, r)
@@ -60,6 +109,9 @@ def test_small_latent_decode_bf16_partials(seed):
 @pytest.mark.parametrize("P,pdt,odt", [(1, torch.float32, torch.bfloat16),
                                         (9, torch.float32, torch.bfloat16),
                                         (9, torch.bfloat16, torch.float32),
+                                        (9, torch.float16, torch.bfloat16),
+                                        (9, torch.float16, torch.float16),
+                                        (2, torch.bfloat16, torch.float16),
                                         (64, torch.float32, torch.float32)])
 def test_lse_combine_random_partials(P, pdt, odt):
     rng = np.random.default_rng(P)

@@ -79,6 +79,29 @@ def test_scaled_batch_million_tokens():
     assert (got[qsl[-1]:] == -1).all()
 
 
+def test_bench_scaled_batch_41m_tokens():
+    """The 41 M-token batch the bench times (20,000 requests, block 16):
+    sampled requests bit-exact against the oracle, every pad slot -1, and every
+    slot of the batch inside the pool and distinct (the tables partition it)."""
+    from workloads.synth import make_slot_batch
+    qsl, pos, bt = make_slot_batch(20000, 1024, 3072, 16, 7)
+    n = int(qsl[-1])
+    M = n + 65536
+    got_t = psw.slot_mapping(i32(qsl), i64(pos), i32(bt), 16, M)
+    pool = int((bt >= 0).sum()) * 16
+    valid = got_t[:n]
+    assert int(valid.min().item()) >= 0 and int(valid.max().item()) < pool
+    assert torch.unique(valid).numel() == n
+    assert bool((got_t[n:] == -1).all())
+    got = got_t.cpu().numpy()
+    rng = np.random.default_rng(41)
+    for r in rng.choice(len(qsl) - 1, 16, replace=False):
+        L = int(qsl[r + 1] - qsl[r])
+        ref = slot_mapping_ref(np.array([0, L], dtype=np.int32), pos[qsl[r]:qsl[r + 1]],
+                               bt[r:r + 1], 16, L)
+        assert np.array_equal(got[qsl[r]:qsl[r + 1]], ref), f"request {r}"
+
+
 @pytest.mark.parametrize("latent", [False, True])
 def test_kv_cache_write_bit_exact(latent):
     w = make_small_case(5, num_seqs=4, max_len=300, hq=8, hkv=2, d=64, block_size=16,

@@ -322,3 +322,20 @@ def make_small_case(seed: int, *, num_seqs=2, max_len=300, hq=4, hkv=2, d=64, dv
     return _assemble(f"small_{seed}", seed, rng, qls, ctxs, block_size, hq, hkv, d, dv, window,
                      causal, chunk[0], chunk[1], ranges, max_ranges, latent=latent,
                      max_num_tokens=int(sum(qls)) + int(rng.integers(0, 64)))
+
+
+def make_slot_batch(num_reqs: int, len_lo: int, len_hi: int, block_size: int, seed: int):
+    """A large slot-mapping batch (not one of the five workloads): request
+    lengths U{len_lo..len_hi}, every position of each request new, block tables
+    a random permutation of an exactly sized pool (unused entries -1).
+    Draw order: lengths, then the permutation.  Returns (query_start_loc int32
+    [R+1], positions int64 [N], block_table int32 [R, stride])."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(len_lo, len_hi + 1, size=num_reqs)
+    bt, _ = _block_tables(rng, lens, block_size)
+    qsl = np.zeros(num_reqs + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(lens)
+    n = int(qsl[-1])
+    # position of token t of request r = t - qsl[r]
+    pos = np.arange(n, dtype=np.int64) - np.repeat(qsl[:-1].astype(np.int64), lens)
+    return qsl, pos, bt
