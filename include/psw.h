@@ -236,6 +236,25 @@ typedef struct psw_attn_args {
 int psw_swa_mm_attention(const psw_attn_args* args, void* stream);
 
 /*
+ * psw_swa_mm_attention_noalloc - psw_swa_mm_attention for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid allocation.  Same arguments, kernels, results and
+ * errors, except that the call's workspace (today only the latent decode uses
+ * one) is a scratch array inside the library instead of args->workspace, which
+ * is ignored with workspace_bytes; the caller still passes inputs and outputs.
+ * The call itself allocates nothing (no hipMalloc / hipFree).
+ * Limit: the scratch holds 130 MiB on each device, enough for the latent decode
+ * with up to 128 query heads per workgroup on 256 CUs and up to 458,751
+ * (token, split) items; a call needing more fails with PSW_ERR_INVALID and a
+ * message, before anything is enqueued.  Every device the library runs on holds its copy of the
+ * scratch from module load until the process ends; nothing in it needs
+ * clearing between calls.  All calls on one device share that device's
+ * scratch: calls that overlap in time on one device (two streams, two host
+ * threads) race, and must be ordered by the caller.
+ */
+int psw_swa_mm_attention_noalloc(const psw_attn_args* args, void* stream);
+
+/*
  * psw_attention_workspace_size - bytes of device workspace psw_swa_mm_attention
  * needs for these arguments on the calling thread's current device (stored in
  * *bytes; 0 when the call needs none).  Today only the latent decode uses it:

@@ -243,8 +243,10 @@ namespace {
 
 // Host checks of one attention call; on PSW_OK, p holds its parameters, latent
 // says which kernel family runs it and empty that there is nothing to launch.
+// With caller_workspace false the call's workspace is the library's scratch
+// instead of args->workspace (which is then ignored).
 int prepare_attention(const psw_attn_args* args, psw::AttnParams& p, bool& latent, bool& empty,
-                      int64_t& workspace_used) {
+                      int64_t& workspace_used, bool caller_workspace = true) {
   int st = fill_geometry(args, p, true);
   if (st != PSW_OK) return st;
   latent = args->v_cache == nullptr;
@@ -256,8 +258,14 @@ int prepare_attention(const psw_attn_args* args, psw::AttnParams& p, bool& laten
                 args->num_splits);
   if (empty) return PSW_OK;
   const int64_t need = workspace_needed(args, p);
-  if (need > 0 && (args->workspace == nullptr || args->workspace_bytes < need ||
-                   (reinterpret_cast<uintptr_t>(args->workspace) & 255) != 0))
+  if (!caller_workspace && need > psw::kScratchBytes)
+    return fail(PSW_ERR_INVALID,
+                "this call needs %lld bytes of scratch; the allocation-free entry point has "
+                "%lld (fewer tokens or splits per call, or psw_swa_mm_attention with a "
+                "workspace)", (long long)need, (long long)psw::kScratchBytes);
+  if (caller_workspace && need > 0 &&
+      (args->workspace == nullptr || args->workspace_bytes < need ||
+       (reinterpret_cast<uintptr_t>(args->workspace) & 255) != 0))
     return fail(PSW_ERR_INVALID,
                 "workspace of %lld bytes (256-byte aligned) required, got %lld at %p",
                 (long long)need, (long long)args->workspace_bytes, args->workspace);
@@ -269,13 +277,18 @@ int prepare_attention(const psw_attn_args* args, psw::AttnParams& p, bool& laten
               p.head_dim_qk, p.head_dim_v, p.queries_per_kv, latent ? "latent" : "separate");
 }
 
-// Enqueues a call that prepare_attention accepted.
+// Enqueues a call that prepare_attention accepted, with `workspace` as its
+// workspace (args->workspace, or the library's scratch).
+int launch_prepared(const psw_attn_args* args, const psw::AttnParams& p, bool latent,
+                    hipStream_t stream, void* workspace) {
+  if (latent && psw::decode_supported(p))
+    return check_hip(psw::launch_attention_decode(p, workspace, stream), "attention(decode)");
+  return check_hip(psw::launch_attention_prefill(p, stream), "attention(prefill)");
+}
+
 int launch_prepared(const psw_attn_args* args, const psw::AttnParams& p, bool latent,
                     hipStream_t stream) {
-  if (latent && psw::decode_supported(p))
-    return check_hip(psw::launch_attention_decode(p, args->workspace, stream),
-                     "attention(decode)");
-  return check_hip(psw::launch_attention_prefill(p, stream), "attention(prefill)");
+  return launch_prepared(args, p, latent, stream, args->workspace);
 }
 
 }  // namespace
@@ -290,6 +303,19 @@ int psw_swa_mm_attention(const psw_attn_args* args, void* stream) {
   if (st != PSW_OK) return st;
   if (empty) return ok();
   return launch_prepared(args, p, latent, (hipStream_t)stream);
+}
+
+int psw_swa_mm_attention_noalloc(const psw_attn_args* args, void* stream) {
+  psw::AttnParams p{};
+  bool latent = false, empty = false;
+  int64_t need = 0;
+  int st = prepare_attention(args, p, latent, empty, need, /*caller_workspace=*/false);
+  if (st != PSW_OK) return st;
+  if (empty) return ok();
+  void* scratch = nullptr;
+  if (need > 0 && (st = check_hip(psw::scratch_device_ptr(&scratch), "scratch address")) != PSW_OK)
+    return st;
+  return launch_prepared(args, p, latent, (hipStream_t)stream, scratch);
 }
 
 int psw_lse_combine(const void* const* partial_out, const float* const* partial_lse,

@@ -40,6 +40,7 @@
 // [256 d, 256 d + 256).
 // The mask (window, image ranges, key range of the split) is applied exactly
 // as in the prefill kernel; one query position per item makes it uniform.
+#include <mutex>
 #include <type_traits>
 
 #include "asm_ops.h"
@@ -907,6 +908,37 @@ hipError_t launch_decode_shape(const AttnParams& p, int heads, const DecodeWork&
 
 int64_t decode_workspace_bytes(const AttnParams& p) {
   return decode_layout(p, decode_grid(p)).bytes;
+}
+
+// Scratch of the allocation-free attention entry point: the latent decode's
+// workspace (tile prefix and the pieces of shared items) at a fixed place in
+// device memory.  Every device the library runs on holds its own copy from
+// module load until the process ends.  Nothing in it needs clearing between
+// calls: the plan kernel writes the whole prefix, and the merge reads only
+// pieces the same call's attention kernel wrote.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_device_ptr(void** ptr) {
+  // In host code `scratch` is only a stand-in for the device symbol: its
+  // address on each device comes from hipGetSymbolAddress, taken once per
+  // device with that device current, and is used instead of the name.
+  constexpr int kMaxDevices = 64;
+  static std::mutex mutex;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mutex);
+  if (addr[dev] == nullptr) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (a == nullptr || (reinterpret_cast<uintptr_t>(a) & 255) != 0) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attention_decode(const AttnParams& p, void* workspace, hipStream_t stream) {

@@ -75,4 +75,9 @@ bool decode_supported(const AttnParams& p);
 int64_t decode_workspace_bytes(const AttnParams& p);
 hipError_t launch_attention_decode(const AttnParams& p, void* workspace, hipStream_t stream);
 
+// Device scratch of the allocation-free entry point (one per device, this many
+// bytes): its address on the current device, looked up on first use.
+constexpr int64_t kScratchBytes = (int64_t)130 << 20;
+hipError_t scratch_device_ptr(void** ptr);
+
 }  // namespace psw

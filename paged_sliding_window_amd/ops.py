@@ -292,6 +292,33 @@ def swa_mm_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[t
     return (out, lse) if (return_lse or num_splits > 1) else out
 
 
+def swa_mm_attention_noalloc(q: torch.Tensor, k_cache: torch.Tensor,
+                             v_cache: Optional[torch.Tensor], block_table: torch.Tensor,
+                             query_start_loc: torch.Tensor, seq_lens: torch.Tensor, *,
+                             out: torch.Tensor, scale: float, window: int, causal: bool,
+                             lse: Optional[torch.Tensor] = None, chunk_size: int = 0,
+                             chunk_lookback: int = -1, mm_ranges: Optional[torch.Tensor] = None,
+                             key_ranges: Optional[torch.Tensor] = None,
+                             head_dim_v: Optional[int] = None, num_splits: Optional[int] = None,
+                             stream=None) -> None:
+    """psw_swa_mm_attention_noalloc: the attention of swa_mm_attention with the
+    workspace taken from the library's own device scratch.  Nothing is
+    allocated here or in the library: ``out`` (and ``lse`` where partials need
+    it) are the caller's; out's dtype is the output type.  Calls that overlap
+    in time on one device share the scratch and must be ordered by the caller."""
+    if out is None:
+        raise ValueError("out is required (this entry point allocates nothing)")
+    if lse is None and (key_ranges is not None or (num_splits or 1) > 1):
+        raise ValueError("partials need lse (this entry point allocates nothing)")
+    a, _, _, _ = _prepare_attention(
+        q, k_cache, v_cache, block_table, query_start_loc, seq_lens, scale=scale, window=window,
+        causal=causal, chunk_size=chunk_size, chunk_lookback=chunk_lookback, mm_ranges=mm_ranges,
+        key_ranges=key_ranges, head_dim_v=head_dim_v, out=out, lse=lse, out_dtype=out.dtype,
+        return_lse=False, num_splits=num_splits, workspace=None, alloc_workspace=False)
+    a.workspace, a.workspace_bytes = None, 0
+    check(load().psw_swa_mm_attention_noalloc(ctypes.byref(a), _stream(stream)))
+
+
 def decode_two_streams(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor],
                        block_table: torch.Tensor, query_start_loc: torch.Tensor,
                        seq_lens: torch.Tensor, *, history_ranges: torch.Tensor,

@@ -256,3 +256,26 @@ def test_combine_shapes():
         check_combine_shapes(10, 64, 639, None)
     with pytest.raises(ValueError):
         check_combine_shapes(10, 64, 640, 9)
+
+
+@no_gpu_only
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    """The allocation-free entry point checks its workspace need against the
+    130 MiB scratch on the host: a latent decode of 4 tokens x 120,000 splits
+    (480,000 items) is refused before anything is launched, 4 x 100,000 fits;
+    a prefill call needs no scratch."""
+    lib = psw.load()
+    fake = 0x100000
+    ptrs = dict(q=fake, k_cache=fake, block_table=fake, query_start_loc=fake, seq_lens=fake,
+                out=fake, lse=fake, key_ranges=fake)
+    big = _latent_decode_args(num_splits=120000, **ptrs)
+    assert lib.psw_swa_mm_attention_noalloc(ctypes.byref(big), None) == PSW_ERR_INVALID
+    assert b"scratch" in lib.psw_last_error()
+    n = ctypes.c_int64()
+    ok = _latent_decode_args(num_splits=100000, **ptrs)
+    assert lib.psw_attention_workspace_size(ctypes.byref(ok), ctypes.byref(n)) == PSW_OK
+    assert 0 < n.value <= 130 << 20
+    assert lib.psw_attention_workspace_size(ctypes.byref(big), ctypes.byref(n)) == PSW_OK
+    assert n.value > 130 << 20
+    # the empty call is accepted with nothing to do
+    assert lib.psw_swa_mm_attention_noalloc(ctypes.byref(_args()), None) == PSW_OK
