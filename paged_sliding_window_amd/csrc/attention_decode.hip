@@ -658,11 +658,13 @@ void decode_full_kernel(const AttnParams p, const DecodeWork wk) {
       }
       const uint32_t kt = smem0 + (uint32_t)(buf * kTileBytes);
 
-      // S^T[32 keys][32 heads] over the 36 k-chunks, K reads KA ahead; with
-      // UNIFORM_BT one DMA instruction of tile t + 2 after every fourth MFMA
+      // S^T[32 keys][32 heads] over the 36 k-chunks, K reads KA ahead (with
+      // one wave per SIMD only the wave's own reads in flight hide the LDS
+      // latency); with UNIFORM_BT one DMA instruction of tile t + 2 after
+      // every fourth MFMA
       f32x16 s;
       {
-        constexpr int N = kKChunks, KA = 3;
+        constexpr int N = kKChunks, KA = 7;
         const uint32_t ka = kt + k_lane;
         bf16x8 kf[KA + 1];
         static_for<KA>([&](auto cc) {
@@ -719,7 +721,7 @@ void decode_full_kernel(const AttnParams p, const DecodeWork wk) {
       // [0, 32), k-chunks 2 b + tr_g) and keys 16 j + [0, 16), j = st / 16;
       // the transposed reads run VA steps ahead
       {
-        constexpr int N = 2 * kOB, VA = 2;
+        constexpr int N = 2 * kOB, VA = 4;
         bf16x4 vr[VA + 1][2];
         auto read_v = [&](auto ss) __attribute__((always_inline)) {
           constexpr int st = decltype(ss)::value;

@@ -18,11 +18,15 @@ namespace psw {
 
 constexpr int kSlotThreads = 256;
 #ifndef SLOT_TPT
-#define SLOT_TPT 4
+#define SLOT_TPT 8
 #endif
 constexpr int kSlotTokensPerThread = SLOT_TPT;  // a multiple of 4
 static_assert(kSlotTokensPerThread % 4 == 0, "whole 16-byte stores");
 constexpr int kWaveLanes = 64;
+#ifndef SLOT_CHUNKS
+#define SLOT_CHUNKS 1
+#endif
+constexpr int kSlotChunks = SLOT_CHUNKS;  // consecutive chunks of 64 x kSlotTokensPerThread per wave
 
 // Largest r in [0, num_reqs) with qsl[r] <= t (qsl non-decreasing, qsl[0] = 0
 // <= t): the candidate interval shrinks 64-fold per round, every lane testing
@@ -91,15 +95,16 @@ __device__ __forceinline__ bool cp_place(uint32_t p, const SlotGeom& g, uint32_t
   }
 }
 
+// One chunk of 64 x kSlotTokensPerThread tokens starting at wave_t0.  r and
+// next carry this lane's request (and the first token of the request after
+// it) from one chunk of the wave to the next; have_r is false until the
+// wave's request has been searched once.
 template <int MODE, bool POW2>
-__global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(
+__device__ __forceinline__ void slot_chunk(
     const int32_t* __restrict__ qsl, int num_reqs, const int64_t* __restrict__ positions,
     int num_tokens, const int32_t* __restrict__ block_table, int stride, int block_size,
-    int32_t* __restrict__ out, int max_num_tokens, const SlotGeom g) {
-  const int lane = threadIdx.x % kWaveLanes;
-  const int64_t wave_t0 = ((int64_t)blockIdx.x * kSlotThreads + (threadIdx.x - lane)) *
-                          kSlotTokensPerThread;
-  if (wave_t0 >= max_num_tokens) return;  // whole wave past the end
+    int32_t* __restrict__ out, int max_num_tokens, const SlotGeom& g, int64_t wave_t0, int lane,
+    int& r, int& next, bool& have_r) {
   const int64_t t0 = wave_t0 + (int64_t)lane * kSlotTokensPerThread;
   int32_t res[kSlotTokensPerThread];
   int64_t pos[kSlotTokensPerThread];
@@ -117,18 +122,72 @@ __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(
     for (int j = 0; j < kSlotTokensPerThread; ++j)
       pos[j] = (t0 + j < num_tokens) ? positions[t0 + j] : 0;
   }
-  // the wave's first token's request (uniform), when it has real tokens
-  int r = (num_reqs > 0 && wave_t0 < num_tokens)
-              ? find_request_wave(qsl, num_reqs, (int)wave_t0, lane)
-              : 0;
+  // the wave's first token's request (uniform), searched once per wave, when
+  // it has real tokens; later chunks continue from each lane's request
+  if (!have_r && num_reqs > 0 && wave_t0 < num_tokens) {
+    r = find_request_wave(qsl, num_reqs, (int)wave_t0, lane);
+    // first token of the next request (kept in a register: read again only
+    // when a lane crosses into it)
+    next = r + 1 < num_reqs ? qsl[r + 1] : INT32_MAX;
+    have_r = true;
+  }
+  bool done = false;
+  if constexpr (MODE == kSlotPlain && POW2) {
+    // Common case: the thread's tokens are all real, inside one request, at
+    // consecutive positions p0 .. p0 + n - 1 below 2^31.  They then span at
+    // most two blocks (n <= block size) or a few, and the table entries of the
+    // first and last are all that is read; anything else takes the general
+    // path below.
+    if (full && num_reqs > 0) {
+      while (t0 >= next) {
+        ++r;
+        next = r + 1 < num_reqs ? qsl[r + 1] : INT32_MAX;
+      }
+      bool run = t0 + kSlotTokensPerThread <= next && pos[0] >= 0 &&
+                 pos[0] + kSlotTokensPerThread - 1 <= INT32_MAX &&
+                 kSlotTokensPerThread <= block_size;
 #pragma unroll
-  for (int j = 0; j < kSlotTokensPerThread; ++j) {
+      for (int j = 1; j < kSlotTokensPerThread; ++j) run = run && pos[j] == pos[0] + j;
+      if (run) {
+        const uint32_t p0 = (uint32_t)pos[0], mask = (uint32_t)(block_size - 1);
+        const uint32_t lb0 = p0 >> g.bs_log2;
+        const uint32_t lb1 = (p0 + kSlotTokensPerThread - 1) >> g.bs_log2;  // lb0 or lb0 + 1
+        const int64_t row = (int64_t)r * stride;
+        const int32_t b0 = lb0 < (uint32_t)stride ? block_table[row + lb0] : -1;
+        const int32_t b1 = lb1 == lb0 ? b0 : (lb1 < (uint32_t)stride ? block_table[row + lb1] : -1);
+#pragma unroll
+        for (int j = 0; j < kSlotTokensPerThread; ++j) {
+          const uint32_t pj = p0 + j;
+          const bool second = (pj >> g.bs_log2) != lb0;
+          const int32_t b = second ? b1 : b0;
+          res[j] = b >= 0 ? (int32_t)(((uint32_t)b << g.bs_log2) + (pj & mask)) : -1;
+        }
+        done = true;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kSlotTokensPerThread && !done; ++j) {
     const int64_t t = t0 + j;
     res[j] = -1;
     if (t < num_tokens && num_reqs > 0) {
-      while (r + 1 < num_reqs && qsl[r + 1] <= t) ++r;  // crossing into the next request
+      while (t >= next) {  // crossing into the next request (empty ones skipped)
+        ++r;
+        next = r + 1 < num_reqs ? qsl[r + 1] : INT32_MAX;
+      }
       const int64_t p = pos[j];
-      if constexpr (MODE == kSlotPlain) {
+      if constexpr (MODE == kSlotPlain && POW2) {
+        // power-of-two blocks: shift and mask of the 32-bit position (the
+        // slot's low 32 bits are those of the 64-bit product below)
+        if (p >= 0 && p <= INT32_MAX) {
+          const uint32_t lb = (uint32_t)p >> g.bs_log2;
+          if (lb < (uint32_t)stride) {
+            const int32_t b = block_table[(int64_t)r * stride + lb];
+            if (b >= 0)
+              res[j] = (int32_t)(((uint32_t)b << g.bs_log2) + ((uint32_t)p & (uint32_t)(block_size - 1)));
+          }
+        }
+      } else if constexpr (MODE == kSlotPlain) {
         if (p >= 0) {
           const int64_t lb = p / block_size;
           if (lb < stride) {
@@ -159,27 +218,37 @@ __global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(
   }
 }
 
+// Each wave maps kSlotChunks consecutive chunks (the request search is done
+// once per wave and carried forward).
+template <int MODE, bool POW2>
+__global__ __launch_bounds__(kSlotThreads) void slot_mapping_kernel(
+    const int32_t* __restrict__ qsl, int num_reqs, const int64_t* __restrict__ positions,
+    int num_tokens, const int32_t* __restrict__ block_table, int stride, int block_size,
+    int32_t* __restrict__ out, int max_num_tokens, const SlotGeom g) {
+  const int lane = threadIdx.x % kWaveLanes;
+  constexpr int64_t kChunkTokens = (int64_t)kWaveLanes * kSlotTokensPerThread;
+  const int64_t wave = (int64_t)blockIdx.x * (kSlotThreads / kWaveLanes) + threadIdx.x / kWaveLanes;
+  int r = 0, next = INT32_MAX;
+  bool have_r = false;
+  for (int c = 0; c < kSlotChunks; ++c) {
+    const int64_t wave_t0 = (wave * kSlotChunks + c) * kChunkTokens;
+    if (wave_t0 >= max_num_tokens) break;  // the rest of the wave's chunks are past the end
+    slot_chunk<MODE, POW2>(qsl, num_reqs, positions, num_tokens, block_table, stride, block_size,
+                           out, max_num_tokens, g, wave_t0, lane, r, next, have_r);
+  }
+}
+
 template <int MODE, bool POW2>
 static hipError_t launch_slot_t(const int32_t* qsl, int num_reqs, const int64_t* positions,
                                 int num_tokens, const int32_t* block_table, int stride,
                                 int block_size, int32_t* out, int max_num_tokens,
                                 const SlotGeom& g, hipStream_t stream) {
-  const int64_t threads = (max_num_tokens + kSlotTokensPerThread - 1) / kSlotTokensPerThread;
-  const int grid = (int)((threads + kSlotThreads - 1) / kSlotThreads);
+  const int64_t per_block = (int64_t)kSlotThreads * kSlotTokensPerThread * kSlotChunks;
+  const int grid = (int)((max_num_tokens + per_block - 1) / per_block);
   hipLaunchKernelGGL((slot_mapping_kernel<MODE, POW2>), dim3(grid), dim3(kSlotThreads), 0, stream,
                      qsl, num_reqs, positions, num_tokens, block_table, stride, block_size, out,
                      max_num_tokens, g);
   return hipGetLastError();
-}
-
-hipError_t launch_slot_mapping(const int32_t* qsl, int num_reqs, const int64_t* positions,
-                               int num_tokens, const int32_t* block_table, int stride,
-                               int block_size, int32_t* out, int max_num_tokens,
-                               hipStream_t stream) {
-  if (max_num_tokens == 0) return hipSuccess;
-  SlotGeom g{};
-  return launch_slot_t<kSlotPlain, false>(qsl, num_reqs, positions, num_tokens, block_table,
-                                          stride, block_size, out, max_num_tokens, g, stream);
 }
 
 static int ilog2_exact(int v) {  // log2 of a power of two, else -1
@@ -188,6 +257,22 @@ static int ilog2_exact(int v) {  // log2 of a power of two, else -1
   while ((1 << l) < v) ++l;
   return l;
 }
+
+hipError_t launch_slot_mapping(const int32_t* qsl, int num_reqs, const int64_t* positions,
+                               int num_tokens, const int32_t* block_table, int stride,
+                               int block_size, int32_t* out, int max_num_tokens,
+                               hipStream_t stream) {
+  if (max_num_tokens == 0) return hipSuccess;
+  SlotGeom g{};
+  g.block_size = block_size;
+  g.bs_log2 = ilog2_exact(block_size);
+  if (g.bs_log2 >= 0)
+    return launch_slot_t<kSlotPlain, true>(qsl, num_reqs, positions, num_tokens, block_table,
+                                           stride, block_size, out, max_num_tokens, g, stream);
+  return launch_slot_t<kSlotPlain, false>(qsl, num_reqs, positions, num_tokens, block_table,
+                                          stride, block_size, out, max_num_tokens, g, stream);
+}
+
 
 hipError_t launch_slot_mapping_cp(const int32_t* qsl, int num_reqs, const int64_t* positions,
                                   int num_tokens, const int32_t* block_table, int stride,
@@ -221,7 +306,7 @@ hipError_t launch_slot_mapping_cp(const int32_t* qsl, int num_reqs, const int64_
   using F = std::false_type;
   if (circular) return g.bs_log2 >= 0 ? go(R{}, T{}) : go(R{}, F{});
   // one rank: the interleave is the identity and the mapping is the plain one
-  if (cp_world_size == 1) return go(P{}, F{});
+  if (cp_world_size == 1) return g.bs_log2 >= 0 ? go(P{}, T{}) : go(P{}, F{});
   return g.pow2 ? go(C{}, T{}) : go(C{}, F{});
 }
 
