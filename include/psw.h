@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define PSW_ABI_VERSION 5
+#define PSW_ABI_VERSION 6
 
 enum psw_status {
   PSW_OK = 0,
@@ -120,7 +120,8 @@ int psw_slot_mapping_cp(const int32_t* query_start_loc, int32_t num_reqs,
  * psw_kv_cache_write - [SLOT] section 1 (the slot id addresses a token's K/V
  * vector in the paged cache).  For every token t with slot s = slot_mapping[t] >= 0:
  *     k_cache[s, h, :] = k_new[t, h, :]   and   v_cache[s, h, :] = v_new[t, h, :]
- * Slots equal to -1 are skipped.
+ * Slots equal to -1 (padding) are skipped, and so is any slot outside
+ * [0, num_slots), which a PSW_DEBUG build also records as failed check 17.
  *   k_new    bf16 [num_tokens, num_kv_heads, head_dim_k]      (device)
  *   v_new    bf16 [num_tokens, num_kv_heads, head_dim_v] or NULL (latent caches
  *            keep V inside K; then v_cache must be NULL too)     (device)
@@ -336,6 +337,23 @@ int psw_decode_two_streams(const psw_attn_args* history, const psw_attn_args* cu
 int psw_tile_bounds(const psw_attn_args* geometry, int32_t tile_size, int32_t block_m,
                     int32_t block_q, const int32_t* seq_idx, const int32_t* q_block_idx,
                     int32_t num_queries, int32_t* out, void* stream);
+
+/*
+ * psw_debug_take_failures - for testing the library itself, not part of the
+ * method.  A build compiled with PSW_DEBUG has its kernels check their internal
+ * invariants (tile ranges inside the request's keys, valid block-table entries
+ * for every tile they load, tile bounds that contain every allowed key, the
+ * request found for each token, KV slots inside the cache, the decode's work
+ * split and workspace pieces) and record each failed check as a bit of a
+ * per-device mask instead of trapping.  This call synchronises the current
+ * device, stores the mask recorded there since the previous call (0 = every
+ * check held; bit i = check i failed, the check list is in the library's
+ * debug_checks.h) in *mask, and clears it.
+ * Errors: PSW_ERR_INVALID for a NULL mask; PSW_ERR_UNSUPPORTED (and *mask = 0)
+ * in builds without PSW_DEBUG; PSW_ERR_HIP if the synchronisation reports an
+ * error.
+ */
+int psw_debug_take_failures(uint32_t* mask);
 
 #ifdef __cplusplus
 }

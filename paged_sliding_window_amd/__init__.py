@@ -6,6 +6,7 @@ checks tensor metadata and passes device pointers and the current stream.
 """
 from .ops import (  # noqa: F401
     attention_workspace_size,
+    debug_take_failures,
     decode_two_streams,
     kv_cache_write,
     lse_combine,

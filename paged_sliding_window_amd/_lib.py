@@ -10,7 +10,10 @@ import os
 
 import torch  # noqa: F401  (loads the HIP runtime libpsw.so links against)
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpsw.so")
+# PSW_LIBRARY selects another build of the same library (the address-sanitizer
+# and PSW_DEBUG variants that build.build_variant makes); unset, the in-tree one.
+LIB_PATH = os.environ.get("PSW_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libpsw.so")
 
 PSW_OK = 0
 PSW_ERR_INVALID = -1
@@ -62,6 +65,7 @@ EXPORTS = {
     "psw_vup_projection": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "psw_tile_bounds": (_i32, [ctypes.POINTER(PswAttnArgs), _i32, _i32, _i32, _vp, _vp, _i32,
                                _vp, _vp]),
+    "psw_debug_take_failures": (_i32, [ctypes.POINTER(ctypes.c_uint32)]),
 }
 
 _lib = None
@@ -73,18 +77,24 @@ class PswError(RuntimeError):
         self.status = status
 
 
+def open_library(path: str) -> ctypes.CDLL:
+    """A handle on the library file at `path` with every export's signature set
+    (load() keeps the process's one handle; this opens another build beside it)."""
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
 def load() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is not built; run paged_sliding_window_amd/build.py "
                               "(or __graft_entry__.build()) first")
-        lib = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in EXPORTS.items():
-            fn = getattr(lib, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = lib
+        _lib = open_library(LIB_PATH)
     return _lib
 
 

@@ -43,9 +43,21 @@ def _torch_lib_dir() -> str:
     return d
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-I", os.path.join(os.path.dirname(HERE), "include"),
+# Variants of the same library (build_variant):
+#   asan:  host code instrumented with AddressSanitizer, device code unchanged;
+#          load it into a process that preloads asan_runtime() (the interpreter
+#          itself is not instrumented)
+#   debug: kernels built with PSW_DEBUG check their internal invariants and
+#          record failed checks (psw_debug_take_failures) instead of trapping
+VARIANTS = {
+    "asan": ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"],
+    "debug": ["-DPSW_DEBUG"],
+}
+
+
+def _compile(src: str, out_dir: str = BUILD, extra: tuple = ()) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src).replace(".hip", ".o"))
+    cmd = [_hipcc(), *HIPCC_FLAGS, *extra, "-I", os.path.join(os.path.dirname(HERE), "include"),
            "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -69,6 +81,58 @@ def build(verbose: bool = True) -> str:
     if verbose:
         print(f"[build] {LIB} ({len(objs)} objects, {ARCH})")
     return LIB
+
+
+def variant_path(kind: str) -> str:
+    """Where build_variant(kind) puts its library: the debug build in-tree beside
+    libpsw.so (GPU runs load it), others under _build/<kind>/."""
+    if kind == "debug":
+        return os.path.join(HERE, "libpsw_debug.so")
+    return os.path.join(BUILD, kind, f"libpsw_{kind}.so")
+
+
+def _clang() -> str:
+    """The clang++ that hipcc drives (ROCm's llvm)."""
+    c = os.path.join(os.path.dirname(os.path.realpath(_hipcc())), "..", "lib", "llvm", "bin",
+                     "clang++")
+    return os.path.normpath(c) if os.path.exists(c) else (shutil.which("clang++") or "clang++")
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime to preload for the asan variant."""
+    r = subprocess.run([_clang(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError(f"AddressSanitizer runtime not found ({path!r})")
+    return path
+
+
+def build_variant(kind: str, verbose: bool = True) -> str:
+    """Compile every source with the variant's extra flags and link it like the
+    release library (the asan variant links the sanitizer runtime shared)."""
+    extra = tuple(VARIANTS[kind])
+    out_dir = os.path.join(BUILD, kind)
+    os.makedirs(out_dir, exist_ok=True)
+    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, out_dir, extra), srcs))
+    tlib = _torch_lib_dir()
+    lib = variant_path(kind)
+    tmp = lib + ".tmp"
+    if kind == "asan":
+        linker = [_clang(), "-fsanitize=address", "-shared-libasan"]
+    else:
+        linker = ["g++"]
+    cmd = [*linker, "-shared", "-o", tmp, *objs, f"-L{tlib}", "-l:libamdhip64.so",
+           f"-Wl,-rpath,{tlib}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link of the {kind} variant failed:\n{r.stderr}")
+    os.replace(tmp, lib)
+    if verbose:
+        print(f"[build] {lib} ({kind} variant, {len(objs)} objects)")
+    return lib
 
 
 if __name__ == "__main__":

@@ -150,7 +150,7 @@ int psw_kv_cache_write(const void* k_new, const void* v_new, const int32_t* slot
                        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
                        slot_mapping, num_tokens, num_kv_heads, head_dim_k, head_dim_v,
                        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
-                       (hipStream_t)stream),
+                       num_slots, (hipStream_t)stream),
                    "kv_cache_write");
 }
 
@@ -477,6 +477,26 @@ int psw_vup_projection(const void* x, const void* w_uv, void* out, int32_t num_t
                                               static_cast<uint16_t*>(out), num_tokens, num_heads,
                                               kv_lora_rank, v_head_dim, (hipStream_t)stream),
                    "vup_projection");
+}
+
+int psw_debug_take_failures(uint32_t* mask) {
+  if (mask == nullptr) return fail(PSW_ERR_INVALID, "mask is NULL");
+  *mask = 0;
+#ifndef PSW_DEBUG
+  return fail(PSW_ERR_UNSUPPORTED, "not a debug build (compile the library with PSW_DEBUG)");
+#else
+  if (const int st = check_hip(hipDeviceSynchronize(), "debug checks (synchronize)"); st != PSW_OK)
+    return st;
+  unsigned total = 0;
+  for (auto take : {psw::debug_take_prefill, psw::debug_take_decode, psw::debug_take_slot_mapping,
+                    psw::debug_take_kv_write}) {
+    unsigned v = 0;
+    if (const int st = check_hip(take(&v), "debug checks (read)"); st != PSW_OK) return st;
+    total |= v;
+  }
+  *mask = total;
+  return ok();
+#endif
 }
 
 int psw_tile_bounds(const psw_attn_args* geometry, int32_t tile_size, int32_t block_m,

@@ -110,6 +110,9 @@ __device__ __forceinline__ DecodeItem decode_item(const AttnParams& p, int item)
     d.t_lo = d.t_hi = 0;
   }
   if (d.t_hi < d.t_lo) d.t_hi = d.t_lo;
+  PSW_DCHECK(8, d.t_lo >= 0 &&
+                    (d.t_lo == d.t_hi || (int64_t)(d.t_hi - 1) * dec::kTile < d.seq_len) &&
+                    (d.row_lo > d.row_hi || (d.row_lo >= 0 && d.row_hi < d.seq_len)));
   return d;
 }
 
@@ -259,6 +262,7 @@ void decode_attention_kernel(const AttnParams p, const DecodeWork wk) {
   int g = g0;
   while (true) {
     const int p0 = wk.prefix[it], p1 = wk.prefix[it + 1];
+    PSW_DCHECK(11, p0 <= p1);
     const DecodeItem d = decode_item<true>(p, it);
     // previous item: all waves done with LDS, all stores and loads retired
     __builtin_amdgcn_s_waitcnt(0);
@@ -300,6 +304,7 @@ void decode_attention_kernel(const AttnParams p, const DecodeWork wk) {
       if constexpr (UNIFORM_BT) {
         // uniform tile base + a per-lane 32-bit offset (row, column half)
         const int blk = load_uniform_i32(bt + (first >> bs_log2));
+        PSW_DCHECK(9, blk >= 0);
         const char* tile_base = reinterpret_cast<const char*>(
             kbase + (((int64_t)blk << bs_log2) + (first & bs_mask)) * slot_pitch);
         const uint32_t row = (uint32_t)min(dma_row, seq_len - 1 - first);
@@ -308,6 +313,7 @@ void decode_attention_kernel(const AttnParams p, const DecodeWork wk) {
       } else {
         const int key = min(first + dma_row, seq_len - 1);
         const int blk = bt[key >> bs_log2];
+        PSW_DCHECK(9, blk >= 0);
         src = kbase + (((int64_t)blk << bs_log2) + (key & bs_mask)) * slot_pitch + dma_hh * 8;
       }
       char* dst = smem + buf * kTileBytes;
@@ -566,6 +572,7 @@ void decode_full_kernel(const AttnParams p, const DecodeWork wk) {
   int g = g0;
   while (true) {
     const int p0 = wk.prefix[it], p1 = wk.prefix[it + 1];
+    PSW_DCHECK(11, p0 <= p1);
     const DecodeItem d = decode_item<true>(p, it);
     // previous item: all waves done with LDS, all stores and loads retired
     __builtin_amdgcn_s_waitcnt(0);
@@ -595,6 +602,7 @@ void decode_full_kernel(const AttnParams p, const DecodeWork wk) {
       const int first = tile * kTile;
       if constexpr (UNIFORM_BT) {
         // uniform block entry blk + a per-lane 32-bit offset (row, column half)
+        PSW_DCHECK(9, blk >= 0);
         const char* tile_base = reinterpret_cast<const char*>(
             kbase + (((int64_t)blk << bs_log2) + (first & bs_mask)) * slot_pitch);
         const uint32_t row = (uint32_t)min(dma_row, seq_len - 1 - first);
@@ -603,6 +611,7 @@ void decode_full_kernel(const AttnParams p, const DecodeWork wk) {
       } else {
         const int key = min(first + dma_row, seq_len - 1);
         const int b = bt[key >> bs_log2];
+        PSW_DCHECK(9, b >= 0);
         return kbase + (((int64_t)b << bs_log2) + (key & bs_mask)) * slot_pitch + dma_hh * 8;
       }
     };
@@ -794,6 +803,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const AttnParams p, c
   const int token = item / p.num_splits, split = item - token * p.num_splits;
   const int64_t orow = ((int64_t)split * p.num_tokens + token) * p.num_q_heads + head;
   const int wf = p0 / per, wl = p1 > p0 ? (p1 - 1) / per : wf;
+  PSW_DCHECK(11, p0 <= p1);
+  PSW_DCHECK(10, p1 <= p0 || (wf >= 0 && wl < G));
   if (p1 > p0 && wf == wl) return;  // written by its workgroup
 
   const int n = p1 > p0 ? wl - wf + 1 : 0;
@@ -967,5 +978,7 @@ hipError_t launch_attention_decode(const AttnParams& p, void* workspace, hipStre
                      p, wk, hpw);
   return hipGetLastError();
 }
+
+PSW_DEBUG_TAKE(debug_take_decode)
 
 }  // namespace psw

@@ -152,6 +152,7 @@ prefill_attention_kernel(const AttnParams p) {
     t_hi = min(t_hi, s_lo + seg);
     t_lo = s_lo;
   }
+  PSW_DCHECK(0, t_lo >= 0 && (t_lo >= t_hi || (int64_t)(t_hi - 1) * S::kTile < seq_len));
 
   // ---- this lane's query row ----------------------------------------------
   const int r = wave * S::kRowsPerWave + (lane & 31);
@@ -170,6 +171,10 @@ prefill_attention_kernel(const AttnParams p) {
       row_hi = (int)hi64;
     }
   }
+  PSW_DCHECK(2, row_lo > row_hi || (row_lo >= 0 && row_hi < seq_len));
+  PSW_DCHECK(3, row_lo > row_hi || (p.key_ranges == nullptr && p.num_splits > 1) ||
+                    ((int64_t)row_lo >= (int64_t)t_lo * S::kTile &&
+                     (int64_t)row_hi < (int64_t)t_hi * S::kTile));
   // The wave's common interval (tiles inside it need no per-element mask) and
   // the union of its rows' intervals (tiles outside it are skipped).
   int wave_lo = row_valid ? row_lo : INT32_MIN, wave_hi = row_valid ? row_hi : INT32_MAX;
@@ -285,6 +290,7 @@ prefill_attention_kernel(const AttnParams p) {
       // instruction row) must fit in 32 bits
       d.fast = first + S::kTile <= seq_len &&
                delta + (int64_t)(S::kTile + S::kInstrPerTile) * pitch + 1024 < ((int64_t)1 << 31);
+      PSW_DCHECK(1, !d.fast || (b0 >= 0 && b1 >= 0));
       const bool lane_far = lane_second ? seg1 > seg0 : seg0 > seg1;
       d.voff = lane_off + (lane_far ? (uint32_t)delta : 0u);
       d.kb = kbase + (d.lo + wave_row);
@@ -323,8 +329,9 @@ prefill_attention_kernel(const AttnParams p) {
         for (int i = 0; i < S::kInstrPerWave; ++i) {
           const int g = wave * S::kInstrPerWave + i;
           const int key = min(first + g + rq, seq_len - 1);
-          const int64_t row = (((int64_t)bt[key >> bs_log2] << bs_log2) + (key & bs_mask)) * pitch +
-                              dma_ch * 16;
+          const int32_t blk = bt[key >> bs_log2];
+          PSW_DCHECK(1, blk >= 0);
+          const int64_t row = (((int64_t)blk << bs_log2) + (key & bs_mask)) * pitch + dma_ch * 16;
           lds_dma16(kbase + row, kt + g * S::kKBlock);
           lds_dma16(vbase + row, vt + g * S::kVBlock);
         }
@@ -526,5 +533,7 @@ hipError_t launch_attention_prefill(const AttnParams& p, hipStream_t stream) {
     default: return hipErrorInvalidValue;
   }
 }
+
+PSW_DEBUG_TAKE(debug_take_prefill)
 
 }  // namespace psw

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "debug_checks.h"
 #include "mask_bounds.h"
 
 namespace psw {
@@ -43,7 +44,7 @@ hipError_t launch_slot_mapping_cp(const int32_t* qsl, int num_reqs, const int64_
 hipError_t launch_kv_cache_write(const uint16_t* k_new, const uint16_t* v_new,
                                  const int32_t* slots, int num_tokens, int num_kv_heads,
                                  int head_dim_k, int head_dim_v, uint16_t* k_cache,
-                                 uint16_t* v_cache, hipStream_t stream);
+                                 uint16_t* v_cache, int64_t num_slots, hipStream_t stream);
 
 constexpr int kMaxPartials = 64;
 struct CombineArgs {
@@ -79,5 +80,13 @@ hipError_t launch_attention_decode(const AttnParams& p, void* workspace, hipStre
 // bytes): its address on the current device, looked up on first use.
 constexpr int64_t kScratchBytes = (int64_t)130 << 20;
 hipError_t scratch_device_ptr(void** ptr);
+
+// Failed debug checks recorded on the current device by each translation
+// unit's kernels since the last call, then cleared (0 outside PSW_DEBUG
+// builds); the caller synchronises the device first.
+hipError_t debug_take_prefill(unsigned* out);
+hipError_t debug_take_decode(unsigned* out);
+hipError_t debug_take_slot_mapping(unsigned* out);
+hipError_t debug_take_kv_write(unsigned* out);
 
 }  // namespace psw

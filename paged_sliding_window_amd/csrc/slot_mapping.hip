@@ -143,6 +143,7 @@ __device__ __forceinline__ void slot_chunk(
         ++r;
         next = r + 1 < num_reqs ? qsl[r + 1] : INT32_MAX;
       }
+      PSW_DCHECK(16, r >= 0 && r < num_reqs && qsl[r] <= t0);
       bool run = t0 + kSlotTokensPerThread <= next && pos[0] >= 0 &&
                  pos[0] + kSlotTokensPerThread - 1 <= INT32_MAX &&
                  kSlotTokensPerThread <= block_size;
@@ -175,6 +176,7 @@ __device__ __forceinline__ void slot_chunk(
         ++r;
         next = r + 1 < num_reqs ? qsl[r + 1] : INT32_MAX;
       }
+      PSW_DCHECK(16, r >= 0 && r < num_reqs && qsl[r] <= t && (r + 1 == num_reqs || t < qsl[r + 1]));
       const int64_t p = pos[j];
       if constexpr (MODE == kSlotPlain && POW2) {
         // power-of-two blocks: shift and mask of the 32-bit position (the
@@ -309,5 +311,7 @@ hipError_t launch_slot_mapping_cp(const int32_t* qsl, int num_reqs, const int64_
   if (cp_world_size == 1) return g.bs_log2 >= 0 ? go(P{}, T{}) : go(P{}, F{});
   return g.pow2 ? go(C{}, T{}) : go(C{}, F{});
 }
+
+PSW_DEBUG_TAKE(debug_take_slot_mapping)
 
 }  // namespace psw

@@ -469,3 +469,13 @@ def tile_bounds(query_start_loc: torch.Tensor, seq_lens: torch.Tensor,
     check(load().psw_tile_bounds(ctypes.byref(a), int(tile_size), int(block_m), int(block_q),
                                  _ptr(seq_idx), _ptr(q_block_idx), n, _ptr(out), _stream(stream)))
     return out
+
+
+def debug_take_failures() -> int:
+    """psw_debug_take_failures: the debug checks that failed on the current
+    device since the previous call (a bit mask, 0 = every check held), then
+    cleared.  Raises PswError (PSW_ERR_UNSUPPORTED) unless the loaded library
+    is a PSW_DEBUG build."""
+    mask = ctypes.c_uint32(0)
+    check(load().psw_debug_take_failures(ctypes.byref(mask)))
+    return int(mask.value)

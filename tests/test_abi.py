@@ -46,9 +46,23 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     lib = psw.load()
-    assert lib.psw_abi_version() == 5
+    assert lib.psw_abi_version() == 6
     assert lib.psw_status_string(PSW_OK) == b"ok"
     assert lib.psw_status_string(PSW_ERR_INVALID) == b"invalid argument"
+
+
+def test_debug_checks_need_a_debug_build():
+    """psw_debug_take_failures: NULL is rejected; a build without PSW_DEBUG
+    answers PSW_ERR_UNSUPPORTED with a zero mask, before touching the device."""
+    from paged_sliding_window_amd import _lib
+    lib = psw.load()
+    assert lib.psw_debug_take_failures(None) == PSW_ERR_INVALID
+    if "debug" not in os.path.basename(_lib.LIB_PATH):
+        m = ctypes.c_uint32(7)
+        assert lib.psw_debug_take_failures(ctypes.byref(m)) == PSW_ERR_UNSUPPORTED
+        assert m.value == 0
+        with pytest.raises(psw.PswError):
+            psw.debug_take_failures()
 
 
 def _args(**kw):
