@@ -123,7 +123,7 @@ def build_variant(kind: str, verbose: bool = True) -> str:
     if kind == "asan":
         linker = [_clang(), "-fsanitize=address", "-shared-libasan"]
     else:
-        linker = ["g++"]
+        linker = ["g++", "-Wl,--no-undefined", "-Wl,-z,defs"]
     cmd = [*linker, "-shared", "-o", tmp, *objs, f"-L{tlib}", "-l:libamdhip64.so",
            f"-Wl,-rpath,{tlib}"]
     r = subprocess.run(cmd, capture_output=True, text=True)
