@@ -76,6 +76,24 @@ def test_random_small_cases(seed):
     _check(gw, out, lse)
 
 
+@pytest.mark.parametrize("seed,d,qpk,bs", [
+    (0, 64, 128, 16),    # the largest GQA ratio: one position per 128-row query block
+    (1, 128, 64, 2),     # two positions per block, two-key cache blocks (per-lane gathers)
+    (2, 256, 5, 32),     # a ratio that does not divide 128: rows 125-127 of a block are idle
+    (3, 64, 16, 128),    # blocks of 128 keys: four tiles per block on the fast path
+    (4, 128, 3, 256),    # blocks of 256 keys
+    (5, 256, 1, 4),      # MHA on four-key blocks
+])
+def test_extreme_gqa_ratios_and_block_sizes(seed, d, qpk, bs):
+    """Parity at the edges of the supported shapes: queries per KV head up to
+    128 (the query block shrinks to 128 / ratio positions, rounded down) and
+    cache blocks from 2 to 256 keys (fast and per-lane tile gathers)."""
+    w = make_small_case(800 + seed, num_seqs=3, max_len=600, hq=qpk, hkv=1, d=d, block_size=bs)
+    gw = GpuWorkload(w)
+    out, lse = gw.attention()
+    _check(gw, out, lse)
+
+
 @pytest.mark.parametrize("seed,pdt", [(0, torch.float32), (1, torch.float32), (2, torch.float16),
                                       (3, torch.bfloat16)])
 def test_key_split_partials(seed, pdt):
