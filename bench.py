@@ -237,14 +237,15 @@ def cpu_baseline(budget_s=45.0):
             "total_s": round(time.perf_counter() - t_start, 1)}
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_attention_gemma16550_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_attention_kv_write_gemma16550_traffic.json")
 PREFILL_SOURCES = ["attention_prefill.hip", "asm_ops.h", "device_common.h", "mask_bounds.h",
                    "psw_internal.h"]
 
 
 def measured_traffic():
-    """HBM bytes per prefill launch from the committed counter runs, or None when
-    the kernel sources differ from the ones the counters were taken on."""
+    """HBM bytes per launch of the prefill kernel with the fused KV-cache write,
+    from the committed counter runs, or None when the kernel sources differ from
+    the ones the counters were taken on."""
     import hashlib
     try:
         rec = json.load(open(TRAFFIC_FILE))
@@ -299,6 +300,21 @@ def main():
           for _ in range(args.steps)]
 
     def prefill_step(i=None):
+        # slot mapping, then one launch that writes the new K/V rows into the
+        # cache and computes the attention (reading the new keys from k_new /
+        # v_new): the same work as the unfused step below, one launch fewer
+        psw.slot_mapping(gw.qsl, gw.positions, gw.block_table, w.block_size, w.max_num_tokens,
+                         out=slots)
+        if i is not None:
+            ev[i][0].record()
+        psw.swa_mm_attention_kv_write(gw.q, k_new, v_new, slots, gw.k_cache, gw.v_cache,
+                                      gw.block_table, gw.qsl, gw.seq_lens, scale=w.scale,
+                                      window=w.window, causal=w.causal, mm_ranges=gw.mm_ranges,
+                                      out=out, lse=lse)
+        if i is not None:
+            ev[i][1].record()
+
+    def unfused_step(i=None):
         psw.slot_mapping(gw.qsl, gw.positions, gw.block_table, w.block_size, w.max_num_tokens,
                          out=slots)
         psw.kv_cache_write(k_new, v_new, slots, gw.k_cache, gw.v_cache)
@@ -310,22 +326,32 @@ def main():
         if i is not None:
             ev[i][1].record()
 
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+
+    def time_steps(step):
+        """(ms per step, mean ms of the timed kernel) over args.steps steps."""
+        t0.record()
+        for i in range(args.steps):
+            step(i)
+        t1.record()
+        torch.cuda.synchronize()
+        return (t0.elapsed_time(t1) / args.steps,
+                sum(a.elapsed_time(b) for a, b in ev) / args.steps)
+
     log("timing prefill")
     for _ in range(args.warmup):
         prefill_step()
     warm_ms = warm(torch, prefill_step, min_ms=args.warm_ms)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(args.steps):
-        prefill_step(i)
-    t1.record()
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    ms_per_step = total_ms / args.steps
-    attn_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    ms_per_step, attn_ms = time_steps(prefill_step)
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (attn_ms * 1e-3) / 1e12
+    log(f"prefill {ms_per_step:.4f} ms/step, fused kernel {attn_ms:.4f} ms")
+
+    log("timing the unfused prefill step")
+    warm(torch, unfused_step, min_ms=args.warm_ms)
+    u_ms, u_attn = time_steps(unfused_step)
+    log(f"unfused {u_ms:.4f} ms/step, attention kernel {u_attn:.4f} ms")
 
     result = {
         "metric": METRIC,
@@ -346,10 +372,11 @@ def main():
             "image_tokens": 256, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim_qk, "block_size": w.block_size,
             "allowed_pairs_per_head": pairs, "flop_per_step": flop,
-            "step": "slot_mapping + kv_cache_write + swa_mm_attention",
+            "step": "slot_mapping + swa_mm_attention_kv_write (KV-cache write fused into the "
+                    "attention launch)",
         },
         "roofline": {
-            "kernel": "prefill attention, head dim 256 (workload 2)",
+            "kernel": "prefill attention with the fused KV-cache write, head dim 256 (workload 2)",
             "bound": "mfma",
             "achieved": round(achieved, 3),
             "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -360,10 +387,18 @@ def main():
             "clock_state": f"steady: {args.warmup} warm-up steps, then {warm_ms:.0f} ms of "
                            "back-to-back steps before the timed ones",
         },
+        "unfused": {
+            "step": "slot_mapping + kv_cache_write + swa_mm_attention",
+            "ms_per_step": round(u_ms, 5),
+            "TFLOPs": round(flop / (u_ms * 1e-3) / 1e12, 3),
+            "attention_kernel_ms": round(u_attn, 5),
+            "attention_kernel_TFLOPs": round(flop / (u_attn * 1e-3) / 1e12, 3),
+            "attention_kernel_frac": round(flop / (u_attn * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "clock_state": f"steady: {args.warm_ms:.0f} ms of back-to-back steps before the timed ones",
+        },
     }
     del gw, k_new, v_new, out, lse
     torch.cuda.empty_cache()
-    log(f"prefill {ms_per_step:.4f} ms/step, attention {attn_ms:.4f} ms")
 
     # ---------------- decode (second half of the path) ----------------
     if not args.skip_decode:

@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define PSW_ABI_VERSION 6
+#define PSW_ABI_VERSION 7
 
 enum psw_status {
   PSW_OK = 0,
@@ -254,6 +254,41 @@ int psw_swa_mm_attention(const psw_attn_args* args, void* stream);
  * threads) race, and must be ordered by the caller.
  */
 int psw_swa_mm_attention_noalloc(const psw_attn_args* args, void* stream);
+
+/*
+ * psw_swa_mm_attention_kv_write - the cache write of psw_kv_cache_write ([SLOT]
+ * section 1) fused into a prefill call of psw_swa_mm_attention: one launch
+ * that stores the new K and V rows in their cache slots and computes the
+ * attention, reading the keys at or past each request's context length from
+ * the new rows instead of the cache (so the attention never waits for the
+ * write).  With the same arguments, the cache afterwards and the outputs are
+ * exactly those of
+ *     psw_kv_cache_write(k_new, v_new, slot_mapping, num_tokens, num_kv_heads,
+ *                        head_dim_qk, head_dim_v, k_cache, v_cache, num_slots)
+ *     psw_swa_mm_attention(args)
+ * when the precondition below holds.
+ *   args          as psw_swa_mm_attention, with separate K and V caches (the
+ *                 prefill shapes); the caches args->k_cache / v_cache are written
+ *   k_new, v_new  bf16 [num_tokens, num_kv_heads, head_dim] (device): row t holds
+ *                 the key / value of new token t
+ *   slot_mapping  int32 [num_tokens] (device): -1 (not stored) or a slot; slots
+ *                 outside [0, num_slots) are skipped (a PSW_DEBUG build records
+ *                 them as failed check 4)
+ *   num_slots     rows of each cache (num_blocks * block_size)
+ * Precondition (beyond psw_swa_mm_attention's): new token i of request r has
+ * slot_mapping[query_start_loc[r] + i] = the slot the block table gives position
+ * context_len + i, as psw_slot_mapping computes it, and no other token shares
+ * it.  The kernel does not check this: a mapping that breaks it still writes
+ * the cache as psw_kv_cache_write would, but the attention reads the new keys
+ * from k_new / v_new, not from wherever the mapping put them.
+ * Errors: psw_swa_mm_attention's; PSW_ERR_UNSUPPORTED for the latent decode
+ * shape (its one new key per request is written with psw_kv_cache_write);
+ * PSW_ERR_INVALID for num_slots < 0 or a NULL k_new, v_new or slot_mapping with
+ * tokens to process.
+ */
+int psw_swa_mm_attention_kv_write(const psw_attn_args* args, const void* k_new,
+                                  const void* v_new, const int32_t* slot_mapping,
+                                  int64_t num_slots, void* stream);
 
 /*
  * psw_attention_workspace_size - bytes of device workspace psw_swa_mm_attention

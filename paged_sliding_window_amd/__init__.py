@@ -13,6 +13,7 @@ from .ops import (  # noqa: F401
     slot_mapping,
     slot_mapping_cp,
     swa_mm_attention,
+    swa_mm_attention_kv_write,
     swa_mm_attention_noalloc,
     tile_bounds,
     vup_projection,

@@ -57,6 +57,8 @@ EXPORTS = {
     "psw_kv_cache_write": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _vp]),
     "psw_swa_mm_attention": (_i32, [ctypes.POINTER(PswAttnArgs), _vp]),
     "psw_swa_mm_attention_noalloc": (_i32, [ctypes.POINTER(PswAttnArgs), _vp]),
+    "psw_swa_mm_attention_kv_write": (_i32, [ctypes.POINTER(PswAttnArgs), _vp, _vp, _vp, _i64,
+                                             _vp]),
     "psw_attention_workspace_size": (_i32, [ctypes.POINTER(PswAttnArgs), ctypes.POINTER(_i64)]),
     "psw_lse_combine": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _i32, _i64, _i32,
                                _vp, _i32, _vp, _vp]),

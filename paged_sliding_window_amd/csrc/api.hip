@@ -318,6 +318,31 @@ int psw_swa_mm_attention_noalloc(const psw_attn_args* args, void* stream) {
   return launch_prepared(args, p, latent, (hipStream_t)stream, scratch);
 }
 
+int psw_swa_mm_attention_kv_write(const psw_attn_args* args, const void* k_new,
+                                  const void* v_new, const int32_t* slot_mapping,
+                                  int64_t num_slots, void* stream) {
+  psw::AttnParams p{};
+  bool latent = false, empty = false;
+  int64_t ws = 0;
+  int st = prepare_attention(args, p, latent, empty, ws);
+  if (st != PSW_OK) return st;
+  if (latent)
+    return fail(PSW_ERR_UNSUPPORTED, "the fused cache write serves the prefill shapes; write a "
+                "latent cache with psw_kv_cache_write");
+  if (num_slots < 0) return fail(PSW_ERR_INVALID, "num_slots %lld < 0", (long long)num_slots);
+  if (empty) return ok();
+  if (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr || args->v_cache == nullptr)
+    return fail(PSW_ERR_INVALID, "k_new, v_new, slot_mapping and v_cache are required");
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.slot_mapping = slot_mapping;
+  p.k_cache_w = const_cast<uint16_t*>(p.k_cache);
+  p.v_cache_w = const_cast<uint16_t*>(p.v_cache);
+  p.num_slots = num_slots;
+  return check_hip(psw::launch_attention_prefill(p, (hipStream_t)stream),
+                   "attention(prefill, cache write)");
+}
+
 int psw_lse_combine(const void* const* partial_out, const float* const* partial_lse,
                     int32_t num_partials, int32_t partial_dtype, int64_t num_rows,
                     int32_t head_dim_v, void* out, int32_t out_dtype, float* out_lse,

@@ -36,7 +36,14 @@
 //     the O rescale is skipped for the whole wave;
 //   * a wave skips tiles outside the union of its rows' allowed intervals, and
 //     masks per element only tiles not inside every row's interval (each row's
-//     allowed keys form one interval).
+//     allowed keys form one interval);
+//   * with the cache write fused in (FUSED), every workgroup reads keys at or
+//     past its request's context length from the new K and V rows rather than
+//     from the cache, so no workgroup waits for another's writes, and the
+//     split-0 workgroup of a query block copies its tokens' new rows of its KV
+//     head into their cache slots ([SLOT] section 1) after its tile loop (the
+//     copy's loads overlap the output stores; copying before the loop instead
+//     measured slower: all resident workgroups then move Q and the copy at once).
 #include <type_traits>
 #include <utility>
 
@@ -98,7 +105,7 @@ __device__ __forceinline__ float dot2_bf16(bf16x2 a, bf16x2 b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
 }
 
-template <class S>
+template <class S, bool FUSED>
 __global__ __launch_bounds__(S::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
 prefill_attention_kernel(const AttnParams p) {
   constexpr int D = S::kD;
@@ -215,6 +222,11 @@ prefill_attention_kernel(const AttnParams p) {
     const char* kbase = reinterpret_cast<const char*>(p.k_cache + (int64_t)kvh * D);
     const char* vbase = reinterpret_cast<const char*>(p.v_cache + (int64_t)kvh * D);
     const int32_t* bt = p.block_table + (int64_t)seq * p.block_table_stride;
+    // Fused cache write: key k >= ctx is row new_row0 + k of k_new / v_new
+    // (rows have a cache slot's pitch)
+    const char* knew = FUSED ? reinterpret_cast<const char*>(p.k_new + (int64_t)kvh * D) : nullptr;
+    const char* vnew = FUSED ? reinterpret_cast<const char*>(p.v_new + (int64_t)kvh * D) : nullptr;
+    const int64_t new_row0 = (int64_t)q_start - ctx;
     const int bs_log2 = p.block_size_log2;
     const int bs_mask = (1 << bs_log2) - 1;
     const float c2 = p.scale_log2;
@@ -232,6 +244,7 @@ prefill_attention_kernel(const AttnParams p) {
     const bool two_segs = bs_log2 == 4;
     const bool lane_second = two_segs && rq >= 16;
     const uint32_t lane_off = (uint32_t)(((two_segs ? (rq & 15) : rq) * pitch) + dma_ch * 16);
+    const uint32_t new_off = (uint32_t)(rq * pitch + dma_ch * 16);  // one run of rows
 
     // Block-table entries of the workgroup's tiles live in two registers:
     // lane l of ent0 / ent1 holds the entry of block blk0 + l / blk0 + 64 + l
@@ -273,8 +286,21 @@ prefill_attention_kernel(const AttnParams p) {
     auto plan_tile = [&](int tile) __attribute__((always_inline)) {
       DmaPlan d;
       d.fast = false;
-      if (!fast_blocks) return d;
       const int first = tile * S::kTile;
+      if constexpr (FUSED) {
+        if (first >= ctx) {
+          // every key of the tile is new: consecutive rows of k_new / v_new
+          d.lo = (new_row0 + first) * pitch;
+          d.voff = new_off;
+          d.fast = first + S::kTile <= seq_len &&
+                   (int64_t)(S::kTile + S::kInstrPerTile) * pitch + 1024 < ((int64_t)1 << 31);
+          d.kb = knew + (d.lo + wave_row);
+          d.vb = vnew + (d.lo + wave_row);
+          return d;
+        }
+        if (first + S::kTile > ctx) return d;  // old and new keys: per-lane path
+      }
+      if (!fast_blocks) return d;
       // with 16-key blocks keys [first, first + 16) sit in block b and the
       // rest in b + 1; larger blocks hold the whole tile
       const int b = first >> bs_log2;
@@ -329,6 +355,12 @@ prefill_attention_kernel(const AttnParams p) {
         for (int i = 0; i < S::kInstrPerWave; ++i) {
           const int g = wave * S::kInstrPerWave + i;
           const int key = min(first + g + rq, seq_len - 1);
+          if (FUSED && key >= ctx) {
+            const int64_t row = (new_row0 + key) * pitch + dma_ch * 16;
+            lds_dma16(knew + row, kt + g * S::kKBlock);
+            lds_dma16(vnew + row, vt + g * S::kVBlock);
+            continue;
+          }
           const int32_t blk = bt[key >> bs_log2];
           PSW_DCHECK(1, blk >= 0);
           const int64_t row = (((int64_t)blk << bs_log2) + (key & bs_mask)) * pitch + dma_ch * 16;
@@ -480,6 +512,57 @@ prefill_attention_kernel(const AttnParams p) {
   // ---- epilogue ------------------------------------------------------------
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // Fused cache write: 16-byte chunk c of this workgroup's copy is chunk
+  // c % (D / 8) of the K (then V) row of token c / (D / 4), KV head kvh.  A
+  // pass moves up to kCopyPass chunks per thread, loaded together; the first
+  // pass's loads are issued before the output stores.
+  constexpr int kCh = D / 8, kCopyPass = D == 256 ? 16 : 8;
+  const int copy_tokens =
+      FUSED && split == 0 ? min(block_q, query_len - q_block * block_q) : 0;
+  const int copy_total = copy_tokens * 2 * kCh;
+  const int64_t copy_tok0 = (int64_t)q_start + q_block * block_q;
+  using CopyBuf = bf16x8[FUSED ? kCopyPass : 1];
+  using CopySlots = int32_t[FUSED ? kCopyPass : 1];
+  auto copy_load = [&](int c0, CopyBuf& cbuf, CopySlots& cslot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kCopyPass; ++i) {
+      const int c = c0 + i * S::kThreads + tid;
+      if (c < copy_total) {
+        const int tok = c / (2 * kCh), rem = c - tok * 2 * kCh;
+        const int64_t elem = ((copy_tok0 + tok) * p.num_kv_heads + kvh) * D + (rem % kCh) * 8;
+        cbuf[i] = *reinterpret_cast<const bf16x8*>((rem < kCh ? p.k_new : p.v_new) + elem);
+        cslot[i] = p.slot_mapping[copy_tok0 + tok];
+      }
+    }
+  };
+  auto copy_store = [&](int c0, const CopyBuf& cbuf, const CopySlots& cslot)
+                        __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kCopyPass; ++i) {
+      const int c = c0 + i * S::kThreads + tid;
+      if (c < copy_total) {
+        const int rem = c % (2 * kCh);
+        const int32_t sl = cslot[i];
+        PSW_DCHECK(4, sl == -1 || (sl >= 0 && sl < p.num_slots));
+        if (sl >= 0 && sl < p.num_slots) {
+          const int64_t elem = ((int64_t)sl * p.num_kv_heads + kvh) * D + (rem % kCh) * 8;
+          *reinterpret_cast<bf16x8*>((rem < kCh ? p.k_cache_w : p.v_cache_w) + elem) = cbuf[i];
+        }
+      }
+    }
+  };
+  auto copy_rest = [&](int c0) __attribute__((always_inline)) {
+    for (; c0 < copy_total; c0 += kCopyPass * S::kThreads) {
+      CopyBuf cb;
+      CopySlots cs;
+      copy_load(c0, cb, cs);
+      copy_store(c0, cb, cs);
+    }
+  };
+  CopyBuf cb;
+  CopySlots cs;
+  if constexpr (FUSED) copy_load(0, cb, cs);
+
   if (row_valid) {
     const int64_t orow = ((int64_t)split * p.num_tokens + token) * p.num_q_heads + head;
     const int64_t e0 = orow * D + half * 4;
@@ -491,6 +574,11 @@ prefill_attention_kernel(const AttnParams p) {
                    o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv);
     if (p.lse != nullptr && half == 0)
       p.lse[orow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+  }
+  if constexpr (FUSED) {
+    copy_store(0, cb, cs);
+    // more passes only with one or two query heads per KV head (64-128 tokens)
+    copy_rest(kCopyPass * S::kThreads);
   }
 }
 
@@ -509,14 +597,14 @@ template <> struct PrefillConfig<64> { using S = PrefillShape<64, 4, 2>; };
 template <> struct PrefillConfig<128> { using S = PrefillShape<128, 4, 2>; };
 template <> struct PrefillConfig<256> { using S = PrefillShape<256, 4, 2>; };
 
-template <int D>
+template <int D, bool FUSED>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
   using S = typename PrefillConfig<D>::S;
   const int block_q = S::kBlockM / p.queries_per_kv;
   const int gx = p.num_tokens / block_q + p.num_seqs;
   if (gx == 0) return hipSuccess;
   const size_t lds = S::kLdsBytes;
-  auto kern = prefill_attention_kernel<S>;
+  auto kern = prefill_attention_kernel<S, FUSED>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
@@ -525,13 +613,19 @@ static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_attention_prefill(const AttnParams& p, hipStream_t stream) {
+template <bool FUSED>
+static hipError_t launch_prefill_d(const AttnParams& p, hipStream_t stream) {
   switch (p.head_dim_qk) {
-    case 64: return launch_prefill_t<64>(p, stream);
-    case 128: return launch_prefill_t<128>(p, stream);
-    case 256: return launch_prefill_t<256>(p, stream);
+    case 64: return launch_prefill_t<64, FUSED>(p, stream);
+    case 128: return launch_prefill_t<128, FUSED>(p, stream);
+    case 256: return launch_prefill_t<256, FUSED>(p, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_attention_prefill(const AttnParams& p, hipStream_t stream) {
+  return p.k_new != nullptr ? launch_prefill_d<true>(p, stream)
+                            : launch_prefill_d<false>(p, stream);
 }
 
 PSW_DEBUG_TAKE(debug_take_prefill)

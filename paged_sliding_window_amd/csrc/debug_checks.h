@@ -17,6 +17,8 @@
 //   3  prefill, unless the tile loop is cut into segmented splits: every valid
 //      row's allowed keys lie inside the workgroup's tile range (the tile
 //      bounds never cut an allowed key)
+//   4  prefill with the fused cache write: a slot other than -1 lies in
+//      [0, num_slots)
 //   8  decode: an item's allowed keys and tile range lie inside its request
 //   9  decode: every block-table entry a tile's loads use is a valid block
 //   10 decode: a piece of a shared item lies inside the workspace's pieces

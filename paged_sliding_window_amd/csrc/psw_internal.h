@@ -27,6 +27,14 @@ struct AttnParams {
   int num_splits;
   int out_dtype;  // kOutBf16, kOutF32 or kOutF16 (the psw_dtype values)
   float scale_log2;  // softmax scale * log2(e)
+  // Cache write fused into the prefill (psw_swa_mm_attention_kv_write); k_new
+  // is nullptr for the plain call.  New rows are [num_tokens, num_kv_heads, D].
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* slot_mapping;
+  uint16_t* k_cache_w;  // the caches, written (same memory as k_cache / v_cache)
+  uint16_t* v_cache_w;
+  int64_t num_slots;
 };
 
 hipError_t launch_slot_mapping(const int32_t* qsl, int num_reqs, const int64_t* positions,

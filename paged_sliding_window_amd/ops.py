@@ -319,6 +319,44 @@ def swa_mm_attention_noalloc(q: torch.Tensor, k_cache: torch.Tensor,
     check(load().psw_swa_mm_attention_noalloc(ctypes.byref(a), _stream(stream)))
 
 
+def swa_mm_attention_kv_write(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                              slots: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              block_table: torch.Tensor, query_start_loc: torch.Tensor,
+                              seq_lens: torch.Tensor, *, scale: float, window: int, causal: bool,
+                              chunk_size: int = 0, chunk_lookback: int = -1,
+                              mm_ranges: Optional[torch.Tensor] = None,
+                              key_ranges: Optional[torch.Tensor] = None,
+                              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                              out_dtype: torch.dtype = torch.bfloat16, return_lse: bool = False,
+                              num_splits: Optional[int] = None, stream=None):
+    """psw_swa_mm_attention_kv_write: kv_cache_write(k_new, v_new, slots, k_cache,
+    v_cache) and swa_mm_attention(...) in one launch (prefill shapes; the new
+    tokens' keys are read from k_new / v_new).  Returns what swa_mm_attention
+    returns."""
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    _need(v_new, "v_new", torch.bfloat16, 3)
+    _need(slots, "slot_mapping", torch.int32, 1)
+    if v_cache is None:
+        raise ValueError("the fused cache write needs separate K and V caches")
+    if k_new.shape[0] != q.shape[0]:
+        raise ValueError(f"k_new has {k_new.shape[0]} rows for {q.shape[0]} query tokens")
+    check_kv_write_shapes(k_new.shape, v_new.shape, slots.numel(), k_cache.shape, v_cache.shape)
+    a, out, lse, _ = _prepare_attention(
+        q, k_cache, v_cache, block_table, query_start_loc, seq_lens, scale=scale, window=window,
+        causal=causal, chunk_size=chunk_size, chunk_lookback=chunk_lookback, mm_ranges=mm_ranges,
+        key_ranges=key_ranges, head_dim_v=None, out=out, lse=lse, out_dtype=out_dtype,
+        return_lse=return_lse, num_splits=num_splits, workspace=None)
+    num_slots = k_cache.shape[0] * k_cache.shape[1]
+    check(load().psw_swa_mm_attention_kv_write(ctypes.byref(a), _ptr(k_new), _ptr(v_new),
+                                               _ptr(slots), num_slots, _stream(stream)))
+    n, hq, dv, num_splits = q.shape[0], q.shape[1], a.head_dim_v, a.num_splits
+    if key_ranges is None and num_splits == 1:
+        out = out.view(n, hq, dv)
+        if lse is not None:
+            lse = lse.view(n, hq)
+    return (out, lse) if (return_lse or num_splits > 1) else out
+
+
 def decode_two_streams(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor],
                        block_table: torch.Tensor, query_start_loc: torch.Tensor,
                        seq_lens: torch.Tensor, *, history_ranges: torch.Tensor,
