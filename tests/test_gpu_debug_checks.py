@@ -180,3 +180,25 @@ def test_debug_random_prefill_sweep(debug_lib):
                 ref_o, ref_l = oracle_rows(w, r)
                 assert_close(out[s0:s0 + ql], ref_o, f"case {i} seq {r}")
                 assert_lse_close(lse[s0:s0 + ql], ref_l, f"case {i} seq {r} lse")
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_debug_fused_cache_write(debug_lib, cfg):
+    """The prefill with the fused cache write through both builds (workload 2
+    as the bench times it, workload 3 with cached context); then one slot past
+    the cache, which both skip and the debug build records as check 4."""
+    from tests.test_gpu_fused_kv_write import FusedCase
+    case = FusedCase(make_config(cfg), spare_blocks=1)
+    ref = case.fused()
+    assert failures(debug_lib) == 0
+    with using(debug_lib):
+        got = case.fused()
+    assert failures(debug_lib) == 0
+    for a, b in zip(ref, got):
+        assert same_bits(a, b)
+    slots = case.slots.clone()
+    slots[0] = case.nb * case.w.block_size
+    with using(debug_lib):
+        k, v, _, _ = case.fused(slots=slots)
+    assert failures(debug_lib) == 1 << 4
+    assert not k[case.nb:].any() and not v[case.nb:].any()
