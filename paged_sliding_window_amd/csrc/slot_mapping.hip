@@ -4,9 +4,11 @@
 // 1024-token tile.  Here the grid is flat over the padded token axis instead:
 // each wave owns 64 x kSlotTokensPerThread consecutive tokens, finds the
 // request of its first token with a 64-way search over query_start_loc (each
-// round one load per lane and a ballot, two rounds for 4096 requests), and
-// each lane then walks forward over the few request boundaries inside its own
-// tokens.  Positions are read with 16-byte loads and slots (or -1) written
+// round one load per lane and a ballot, two rounds for 4096 requests); each
+// lane then moves to its own first token's request (one step for the usual
+// case of one boundary, a galloping search when many short requests lie in
+// between, as in decode batches of one token per request) and crosses the
+// boundaries inside its own tokens with the next few boundaries read ahead.  Positions are read with 16-byte loads and slots (or -1) written
 // with 16-byte stores, so every wave streams contiguous positions and slots.
 // Block-table entries are read per token; consecutive tokens of a request hit
 // the same cache line, which plays the role of the page's bounded window.
@@ -45,6 +47,46 @@ __device__ __forceinline__ int find_request_wave(const int32_t* __restrict__ qsl
     lo = nlo;
   }
   return lo;
+}
+
+// Moves r forward to the request of token t, given qsl[r] <= t and next =
+// qsl[r + 1] (INT32_MAX past the last request); empty requests are skipped.
+// One step covers the usual case of at most one boundary; past that the
+// search gallops (probing r + 2, r + 3, r + 5, ...) and then halves, so a
+// lane k requests past the wave's first one pays O(log k) dependent loads.
+__device__ __forceinline__ void seek_request(const int32_t* __restrict__ qsl, int num_reqs,
+                                             int64_t t, int& r, int& next) {
+  if (t < next) return;
+  ++r;  // qsl[r] = next <= t
+  next = r + 1 < num_reqs ? qsl[r + 1] : INT32_MAX;
+  if (t < next) return;
+  // invariant: qsl[lo] <= t < v_hi = qsl[hi] (hi == num_reqs: past the end)
+  int lo = r + 1, step = 1, hi, v_hi = INT32_MAX;
+  for (;;) {
+    hi = lo + step;
+    if (hi >= num_reqs) {
+      hi = num_reqs;
+      break;
+    }
+    const int v = qsl[hi];
+    if (v > t) {
+      v_hi = v;
+      break;
+    }
+    lo = hi;
+    step <<= 1;
+  }
+  while (hi - lo > 1) {
+    const int mid = lo + ((hi - lo) >> 1);
+    const int v = qsl[mid];
+    if (v <= t) lo = mid;
+    else {
+      hi = mid;
+      v_hi = v;
+    }
+  }
+  r = lo;
+  next = v_hi;
 }
 
 // Geometry of the context-parallel and circular modes ([SLOT] sections 2.2,
@@ -131,6 +173,8 @@ __device__ __forceinline__ void slot_chunk(
     next = r + 1 < num_reqs ? qsl[r + 1] : INT32_MAX;
     have_r = true;
   }
+  // this lane's first token's request
+  if (num_reqs > 0 && have_r && t0 < num_tokens) seek_request(qsl, num_reqs, t0, r, next);
   bool done = false;
   if constexpr (MODE == kSlotPlain && POW2) {
     // Common case: the thread's tokens are all real, inside one request, at
@@ -139,10 +183,6 @@ __device__ __forceinline__ void slot_chunk(
     // first and last are all that is read; anything else takes the general
     // path below.
     if (full && num_reqs > 0) {
-      while (t0 >= next) {
-        ++r;
-        next = r + 1 < num_reqs ? qsl[r + 1] : INT32_MAX;
-      }
       PSW_DCHECK(16, r >= 0 && r < num_reqs && qsl[r] <= t0);
       bool run = t0 + kSlotTokensPerThread <= next && pos[0] >= 0 &&
                  pos[0] + kSlotTokensPerThread - 1 <= INT32_MAX &&
@@ -167,6 +207,16 @@ __device__ __forceinline__ void slot_chunk(
       }
     }
   }
+  // General path: the lane's next boundaries qsl[rw + 1 + k], read together,
+  // serve its tokens' crossings (one token per request needs one per token);
+  // more crossings than that (empty requests) read on
+  int32_t win[kSlotTokensPerThread];
+  const int rw = r;
+  if (!done && num_reqs > 0 && t0 < num_tokens) {
+#pragma unroll
+    for (int k = 0; k < kSlotTokensPerThread; ++k)
+      win[k] = rw + 1 + k < num_reqs ? qsl[rw + 1 + k] : INT32_MAX;
+  }
 #pragma unroll
   for (int j = 0; j < kSlotTokensPerThread && !done; ++j) {
     const int64_t t = t0 + j;
@@ -174,7 +224,15 @@ __device__ __forceinline__ void slot_chunk(
     if (t < num_tokens && num_reqs > 0) {
       while (t >= next) {  // crossing into the next request (empty ones skipped)
         ++r;
-        next = r + 1 < num_reqs ? qsl[r + 1] : INT32_MAX;
+        const int k = r - rw;  // >= 1
+        int32_t nx = INT32_MAX;
+        if (k < kSlotTokensPerThread) {
+#pragma unroll
+          for (int i = 1; i < kSlotTokensPerThread; ++i) nx = k == i ? win[i] : nx;
+        } else {
+          nx = r + 1 < num_reqs ? qsl[r + 1] : INT32_MAX;
+        }
+        next = nx;
       }
       PSW_DCHECK(16, r >= 0 && r < num_reqs && qsl[r] <= t && (r + 1 == num_reqs || t < qsl[r + 1]));
       const int64_t p = pos[j];

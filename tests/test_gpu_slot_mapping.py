@@ -130,8 +130,9 @@ def test_kv_cache_write_bit_exact(latent):
 @pytest.mark.parametrize("R", [1, 2, 63, 64, 65, 4095, 4096, 4097, 20000])
 def test_request_search_across_counts(R):
     """Many short and empty requests: the request of each token is found by a
-    64-way search per wave (one to three rounds over these counts) and then a
-    per-lane walk across the request boundaries inside the lane's tokens."""
+    64-way search per wave (one to three rounds over these counts), then per
+    lane a galloping search to the lane's first token and the read-ahead
+    boundaries across the lane's own tokens."""
     rng = np.random.default_rng(1000 + R)
     B = 16
     lens = rng.integers(0, 9, size=R) * (rng.random(R) > 0.3)
@@ -141,6 +142,25 @@ def test_request_search_across_counts(R):
     N = int(qsl[-1])
     pos = rng.integers(0, stride * B, size=N).astype(np.int64)
     M = N + 37
+    got = _gpu_slots(qsl, pos, bt, B, M)
+    ref = slot_mapping_ref(qsl, pos, bt, B, M)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("R", [64, 511, 4096])
+@pytest.mark.parametrize("B", [16, 64])
+def test_decode_shaped_batches(R, B):
+    """Decode batches: one new token per request at a late position (some
+    requests empty), so a lane's first token lies up to several hundred
+    requests past its wave's first one."""
+    rng = np.random.default_rng(77 + R + B)
+    lens = (rng.random(R) > 0.1).astype(np.int64)
+    stride = 32768 // B + 1
+    bt = rng.permutation(R * stride).reshape(R, stride).astype(np.int32)
+    qsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N = int(qsl[-1])
+    pos = rng.integers(0, 32768, size=N).astype(np.int64)
+    M = N + 5
     got = _gpu_slots(qsl, pos, bt, B, M)
     ref = slot_mapping_ref(qsl, pos, bt, B, M)
     assert np.array_equal(got, ref)
