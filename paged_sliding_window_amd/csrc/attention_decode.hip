@@ -913,7 +913,10 @@ template <bool UNIFORM_BT>
 hipError_t launch_decode_shape(const AttnParams& p, int heads, const DecodeWork& wk,
                                hipStream_t stream) {
   if (heads == 128) return launch_decode_full<UNIFORM_BT>(p, wk, stream);
-  if (heads == 64) return launch_decode_t<2, 1, UNIFORM_BT>(p, wk, stream);
+  // 64 heads as two 32-head groups of two waves each: one group of 64 heads per
+  // wave pair needs more than the register file and spills inside its loop
+  // (4x slower when measured)
+  if (heads == 64) return launch_decode_t<1, 2, UNIFORM_BT>(p, wk, stream);
   return launch_decode_t<1, 1, UNIFORM_BT>(p, wk, stream);
 }
 
