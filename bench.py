@@ -411,6 +411,8 @@ def main():
         result["prefill_segmented"] = bench_segmented(args, torch, psw)
         log("slot mapping, scaled batch")
         result["slot_mapping_scaled"] = bench_slot_mapping(args, torch, psw, np)
+        log("library GEMM ceiling")
+        result["library_gemm_ceiling"] = bench_gemm_ceiling(args, torch, achieved)
     if not args.skip_cpu:
         log("CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline()
@@ -451,6 +453,42 @@ def bench_prefill_configs(args, torch, psw):
         del gw, out, lse
         torch.cuda.empty_cache()
     return res
+
+
+def bench_gemm_ceiling(args, torch, attn_tflops, reps=10):
+    """What a plain library bf16 GEMM (torch.matmul on hipBLASLt, then on
+    rocBLAS) reaches on this GPU at steady clocks: the practical matrix-core
+    rate that an attention kernel's fraction of the published peak can be read
+    against.  Context only; no step of the path uses it."""
+    best = None
+    backends = []
+    for lib in ("cublaslt", "cublas"):  # hipBLASLt and rocBLAS under ROCm
+        try:
+            torch.backends.cuda.preferred_blas_library(lib)
+            backends.append(lib)
+        except Exception:  # noqa: BLE001  (a backend this build lacks is skipped)
+            continue
+        for m, n, k in ((8192, 8192, 8192), (16384, 8192, 8192), (16384, 16384, 8192)):
+            a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16)
+            b = torch.randn(k, n, device="cuda", dtype=torch.bfloat16)
+            c = torch.empty(m, n, device="cuda", dtype=torch.bfloat16)
+            fn = lambda: torch.matmul(a, b, out=c)  # noqa: E731
+            warm(torch, fn, min_ms=args.warm_ms)
+            ms = timed_events(torch, fn, reps, rounds=3)
+            tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+            if best is None or tf > best["TFLOPs"]:
+                best = {"shape_mnk": [m, n, k], "ms": round(ms, 4), "TFLOPs": round(tf, 1),
+                        "library": {"cublaslt": "hipBLASLt", "cublas": "rocBLAS"}[lib]}
+            del a, b, c
+    torch.backends.cuda.preferred_blas_library("default")
+    torch.cuda.empty_cache()
+    if best is None:
+        return None
+    best["what"] = ("torch.matmul bf16 in, fp32 accumulate, bf16 out; best of three shapes "
+                    "on each BLAS backend tried: " + ", ".join(backends))
+    best["frac_of_mfma_peak"] = round(best["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4)
+    best["prefill_kernel_frac_of_gemm"] = round(attn_tflops / best["TFLOPs"], 4)
+    return best
 
 
 def bench_segmented(args, torch, psw, splits=4, reps=20):
