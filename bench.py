@@ -298,6 +298,7 @@ def main():
     lse = torch.empty((w.num_tokens, w.num_q_heads), dtype=torch.float32, device="cuda")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    ev_kv = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
     def prefill_step(i=None):
         # slot mapping, then one launch that writes the new K/V rows into the
@@ -317,6 +318,8 @@ def main():
     def unfused_step(i=None):
         psw.slot_mapping(gw.qsl, gw.positions, gw.block_table, w.block_size, w.max_num_tokens,
                          out=slots)
+        if i is not None:
+            ev_kv[i].record()
         psw.kv_cache_write(k_new, v_new, slots, gw.k_cache, gw.v_cache)
         if i is not None:
             ev[i][0].record()
@@ -351,6 +354,9 @@ def main():
     log("timing the unfused prefill step")
     warm(torch, unfused_step, min_ms=args.warm_ms)
     u_ms, u_attn = time_steps(unfused_step)
+    kv_ms = sum(a.elapsed_time(b[0]) for a, b in zip(ev_kv, ev)) / args.steps
+    # each new row read once and written once, K and V
+    kv_bytes = 2 * 2 * k_new.numel() * k_new.element_size() + w.num_tokens * 4
     log(f"unfused {u_ms:.4f} ms/step, attention kernel {u_attn:.4f} ms")
 
     result = {
@@ -394,6 +400,10 @@ def main():
             "attention_kernel_ms": round(u_attn, 5),
             "attention_kernel_TFLOPs": round(flop / (u_attn * 1e-3) / 1e12, 3),
             "attention_kernel_frac": round(flop / (u_attn * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "kv_cache_write": {"ms": round(kv_ms, 5), "bytes": kv_bytes,
+                               "GBps": round(kv_bytes / (kv_ms * 1e-3) / 1e9, 1),
+                               "what": "new K and V rows read and written to their slots, "
+                                       "slots read"},
             "clock_state": f"steady: {args.warm_ms:.0f} ms of back-to-back steps before the timed ones",
         },
     }
@@ -630,6 +640,8 @@ def bench_decode(args, torch, psw, np):
     vup_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
     vup_bytes = ds.out.numel() * 2 + ds.w_uv.numel() * 2 + ds.vup_out.numel() * 2
     kv_bytes = int(w.seq_lens.sum()) * w.head_dim_qk * 2
+    comb_bytes = (ds.part_o.numel() * ds.part_o.element_size() + ds.part_l.numel() * 4
+                  + ds.out.numel() * 2 + ds.out_lse.numel() * 4)
     # KV rows once + Q + block table + W_UV + the projected output (the merged
     # latent output is an intermediate)
     alg_bytes = (kv_bytes + ds.q.numel() * 2 + w.block_table.size * 4 + ds.w_uv.numel() * 2
@@ -647,6 +659,10 @@ def bench_decode(args, torch, psw, np):
         "attention_GBps": round(attn_gbs, 1),
         "attention_frac_of_hbm_peak": round(attn_gbs / HBM_PEAK_GBS, 4),
         "combine_ms": round(comb_ms, 5),
+        "combine": {"ms": round(comb_ms, 5), "bytes": comb_bytes,
+                    "GBps": round(comb_bytes / (comb_ms * 1e-3) / 1e9, 1),
+                    "what": f"{ds.P} partials ({args.decode_partials}) + their LSEs read, "
+                            "bf16 output + fp32 LSE written"},
         "vup_projection": {"ms": round(vup_ms, 5), "algorithmic_bytes": vup_bytes,
                            "GBps": round(vup_bytes / (vup_ms * 1e-3) / 1e9, 1),
                            "shape": f"[{R}, {H}, {DV}] x [{H}, {DV}, {ds.dv_up}]"},

@@ -1,22 +1,33 @@
 """Per-query-block KV tile interval that can hold any allowed key.
 
-Follows [SWA-MM] "Implementation breakdown" items 1-2 and "Key source snippet"
-(the union bounds of ``compute_tile_loop_bounds``):
+[SWA-MM] "Implementation breakdown" items 1-2: with image ranges in the mask,
+the tile loop of a query block must still skip tiles outside the window, so
+its bounds become the union of the window interval of the block's rows and
+the keys that any image range holding one of those rows opens up, each range
+clamped on the left by the window of the row it reaches from.  Stated here
+in terms of the block's rows:
 
   rows of the block: positions qpos_lo = q_block * BLOCK_Q up to
     qpos_hi = qpos_lo + (BLOCK_M - 1) // queries_per_kv, clamped to the
     request's last new token; absolute q = context_len + qpos.
-  pruning applies only with a sliding window (the image ranges here are always
-    window-clamped, and the reverse-window variant is not supported):
-    first key = chunk-lookback edge of the block's first row when lookback >= 0,
-                else first row - W + 1;
-    last key  = last row (causal) or last row + W - 1 (non-causal right window);
-    every valid image range that intersects the block's rows lowers first to
-      max(range start, first row - W + 1) and raises last to the range end;
-    last is clamped to seq_len - 1 when image ranges are in use;
-    tiles = [max(0, first // T), min(last // T + 1, num_tiles)).
-  without a window the interval is [0, num_tiles).
-  num_tiles = ceil(max_seq_prefix_len / T).
+  window part: consecutive rows slide the same window, so their union runs
+    from the lower edge of the first row (q_lo - W + 1, or with chunk
+    lookback the chunk edge of the first row, the page's choice; it ignores
+    the window there) to the upper edge of the last row (q_hi causal,
+    q_hi + W - 1 with the non-causal right window).
+  image part: a valid range [s, e] that holds a row of the block lets that
+    row see keys up to e and down to max(s, q - W + 1), so it widens the
+    union to [max(s, q_lo - W + 1), e]; with image ranges the upper end is
+    kept below seq_len.
+  tiles = [max(0, first // T), min(last // T + 1, num_tiles)),
+  num_tiles = ceil(max_seq_prefix_len / T); without a window nothing is
+  pruned: [0, num_tiles).
+
+tests/test_oracle_tile_bounds.py checks this against the mask's definition
+directly (1,500 random geometries: every allowed key of every row lies inside
+the interval, and the interval is exactly the tile hull of the allowed keys
+wherever the chunk-edge choice does not widen it) and against the printed
+geometries.
 
 Readings where the page is silent or unsafe as printed:
   * The page computes the base lower bound from the block's LAST row.  That
