@@ -167,10 +167,28 @@ __device__ __forceinline__ void slot_chunk(
   // the wave's first token's request (uniform), searched once per wave, when
   // it has real tokens; later chunks continue from each lane's request
   if (!have_r && num_reqs > 0 && wave_t0 < num_tokens) {
+    // (uniform branch: every lane of the wave takes it)
     r = find_request_wave(qsl, num_reqs, (int)wave_t0, lane);
-    // first token of the next request (kept in a register: read again only
-    // when a lane crosses into it)
-    next = r + 1 < num_reqs ? qsl[r + 1] : INT32_MAX;
+    // The 64 boundaries after it, one per lane, in one load: a lane whose
+    // first token lies within them finds its request by a binary search over
+    // the lanes (the boundaries are non-decreasing), so batches of short
+    // requests, such as decode steps of one token per request, need no chain
+    // of dependent loads.  `next` is the first token of the request after the
+    // lane's (kept in a register: read again only when a lane crosses into it).
+    const int wj = r + 1 + lane;
+    const int32_t wq = wj < num_reqs ? qsl[wj] : INT32_MAX;
+    int cnt = 0;  // boundaries of the window at or below t0 (a prefix of it)
+#pragma unroll
+    for (int step = 32; step > 0; step >>= 1) {
+      const int32_t v = __shfl(wq, cnt + step - 1, kWaveLanes);
+      if ((int64_t)v <= t0) cnt += step;
+    }
+    const int32_t last = __shfl(wq, kWaveLanes - 1, kWaveLanes);
+    if (cnt == kWaveLanes - 1 && (int64_t)last <= t0) cnt = kWaveLanes;
+    const int32_t nx = __shfl(wq, cnt & (kWaveLanes - 1), kWaveLanes);
+    r += cnt;
+    if (cnt < kWaveLanes) next = nx;
+    else next = r + 1 < num_reqs ? qsl[r + 1] : INT32_MAX;  // past the window: read on
     have_r = true;
   }
   // this lane's first token's request
