@@ -636,18 +636,36 @@ def bench_decode(args, torch, psw, np):
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
     attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    comb_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
-    vup_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
-    vup_bytes = ds.out.numel() * 2 + ds.w_uv.numel() * 2 + ds.vup_out.numel() * 2
+    tail_ms = sum(e[1].elapsed_time(e[3]) for e in ev) / steps
     kv_bytes = int(w.seq_lens.sum()) * w.head_dim_qk * 2
-    comb_bytes = (ds.part_o.numel() * ds.part_o.element_size() + ds.part_l.numel() * 4
-                  + ds.out.numel() * 2 + ds.out_lse.numel() * 4)
+    part_bytes = ds.part_o.numel() * ds.part_o.element_size() + ds.part_l.numel() * 4
+    # the tail reads the partials and W_UV and writes the projected output, the
+    # merged rows and their LSEs
+    tail_bytes = (part_bytes + ds.w_uv.numel() * 2 + ds.vup_out.numel() * 2 + ds.out.numel() * 2
+                  + ds.out_lse.numel() * 4)
     # KV rows once + Q + block table + W_UV + the projected output (the merged
     # latent output is an intermediate)
     alg_bytes = (kv_bytes + ds.q.numel() * 2 + w.block_table.size * 4 + ds.w_uv.numel() * 2
                  + ds.vup_out.numel() * 2)
     gbs = alg_bytes / (ms * 1e-3) / 1e9
     attn_gbs = (kv_bytes + ds.q.numel() * 2) / (attn_ms * 1e-3) / 1e9
+    # the same tail as two launches (combine, then projection), timed apart
+    comb_bytes = part_bytes + ds.out.numel() * 2 + ds.out_lse.numel() * 4
+    vup_bytes = ds.out.numel() * 2 + ds.w_uv.numel() * 2 + ds.vup_out.numel() * 2
+    warm(torch, ds.combine, min_ms=args.warm_ms / 4)
+    comb_ms = timed_events(torch, ds.combine, 20)
+    vup = lambda: psw.vup_projection(ds.out, ds.w_uv, out=ds.vup_out)  # noqa: E731
+    warm(torch, vup, min_ms=args.warm_ms / 4)
+    vup_ms = timed_events(torch, vup, 20)
+
+    def two_tail():
+        ds.combine()
+        vup()
+    warm(torch, two_tail, min_ms=args.warm_ms / 4)
+    two_tail_ms = timed_events(torch, two_tail, 20)
+    step_two = lambda: ds.run(fused_tail=False)  # noqa: E731
+    warm(torch, step_two, min_ms=args.warm_ms / 2)
+    step_two_ms = timed_events(torch, step_two, steps, rounds=3)
     res = {
         "workload": "mla_splitkv_decode_b64",
         "unit": "GB/s",
@@ -658,20 +676,25 @@ def bench_decode(args, torch, psw, np):
         "attention_ms": round(attn_ms, 5),
         "attention_GBps": round(attn_gbs, 1),
         "attention_frac_of_hbm_peak": round(attn_gbs / HBM_PEAK_GBS, 4),
-        "combine_ms": round(comb_ms, 5),
-        "combine": {"ms": round(comb_ms, 5), "bytes": comb_bytes,
-                    "GBps": round(comb_bytes / (comb_ms * 1e-3) / 1e9, 1),
-                    "what": f"{ds.P} partials ({args.decode_partials}) + their LSEs read, "
-                            "bf16 output + fp32 LSE written"},
-        "vup_projection": {"ms": round(vup_ms, 5), "algorithmic_bytes": vup_bytes,
-                           "GBps": round(vup_bytes / (vup_ms * 1e-3) / 1e9, 1),
-                           "shape": f"[{R}, {H}, {DV}] x [{H}, {DV}, {ds.dv_up}]"},
+        "combine_vup": {"ms": round(tail_ms, 5), "bytes": tail_bytes,
+                        "GBps": round(tail_bytes / (tail_ms * 1e-3) / 1e9, 1),
+                        "what": f"lse_combine_vup: {ds.P} partials ({args.decode_partials}) "
+                                "merged and projected in one launch (merged rows and LSEs "
+                                "written too)"},
+        "tail_as_two_launches": {
+            "ms": round(two_tail_ms, 5),
+            "step_ms": round(step_two_ms, 5),
+            "combine": {"ms": round(comb_ms, 5), "bytes": comb_bytes,
+                        "GBps": round(comb_bytes / (comb_ms * 1e-3) / 1e9, 1)},
+            "vup_projection": {"ms": round(vup_ms, 5), "bytes": vup_bytes,
+                               "GBps": round(vup_bytes / (vup_ms * 1e-3) / 1e9, 1),
+                               "shape": f"[{R}, {H}, {DV}] x [{H}, {DV}, {ds.dv_up}]"}},
         "history_splits": ds.S,
         "partials": ds.P,
         "partial_dtype": args.decode_partials,
         "clock_state": f"steady: {warm_ms:.0f} ms of back-to-back steps before the timed ones",
         "step": "slot_mapping + kv_cache_write + history and current partials (one call) "
-                "+ lse_combine + vup_projection",
+                "+ lse_combine_vup (LSE combine and V-up projection in one launch)",
     }
     if two is not None:
         res["two_streams"] = two

@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define PSW_ABI_VERSION 7
+#define PSW_ABI_VERSION 8
 
 enum psw_status {
   PSW_OK = 0,
@@ -153,6 +153,33 @@ int psw_kv_cache_write(const void* k_new, const void* v_new, const int32_t* slot
 int psw_vup_projection(const void* x, const void* w_uv, void* out, int32_t num_tokens,
                        int32_t num_heads, int32_t kv_lora_rank, int32_t v_head_dim,
                        void* stream);
+
+/*
+ * psw_lse_combine_vup - the two steps that end the latent decode in one launch:
+ * the LSE merge of psw_lse_combine ([DCP] "Terms", section 1.1, code block D)
+ * over P partial latent outputs, then the V-up projection of psw_vup_projection
+ * ([DCP] "Terms", section 1.1, code block A) of the merged rows:
+ *     x[t, h, :] = sum_p w_p O_p[t, h, :] / sum_p w_p,   out[t, h, :] = x[t, h, :] @ w_uv[h]
+ * Results are bit for bit those of psw_lse_combine (bf16 output) followed by
+ * psw_vup_projection on its output; the merged rows are only written when
+ * merged != NULL.
+ *   partial_out  host array of P device pointers, each partial_dtype
+ *                [num_tokens, num_heads, kv_lora_rank] (PSW_BF16, PSW_F16 or PSW_F32)
+ *   partial_lse  host array of P device pointers, each fp32 [num_tokens, num_heads]
+ *   w_uv         bf16 [num_heads, kv_lora_rank, v_head_dim] (device)
+ *   out          bf16 [num_tokens, num_heads, v_head_dim] (device), caller-owned
+ *   out_lse      fp32 [num_tokens, num_heads] or NULL: LSE of each merged row
+ *   merged       bf16 [num_tokens, num_heads, kv_lora_rank] or NULL: the merged rows
+ * The partials are read in place.  Errors: PSW_ERR_INVALID for P outside
+ * [1, 16], negative sizes, an unknown dtype or a NULL pointer with work to do;
+ * PSW_ERR_UNSUPPORTED unless kv_lora_rank is 128, 256 or 512 and v_head_dim is
+ * a positive multiple of 64.
+ */
+int psw_lse_combine_vup(const void* const* partial_out, const float* const* partial_lse,
+                        int32_t num_partials, int32_t partial_dtype, const void* w_uv,
+                        void* out, float* out_lse, void* merged, int32_t num_tokens,
+                        int32_t num_heads, int32_t kv_lora_rank, int32_t v_head_dim,
+                        void* stream);
 
 /*
  * Arguments of psw_swa_mm_attention and psw_tile_bounds.

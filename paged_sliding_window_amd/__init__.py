@@ -10,6 +10,7 @@ from .ops import (  # noqa: F401
     decode_two_streams,
     kv_cache_write,
     lse_combine,
+    lse_combine_vup,
     slot_mapping,
     slot_mapping_cp,
     swa_mm_attention,

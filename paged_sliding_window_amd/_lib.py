@@ -65,6 +65,8 @@ EXPORTS = {
     "psw_decode_two_streams": (_i32, [ctypes.POINTER(PswAttnArgs), ctypes.POINTER(PswAttnArgs), _vp,
                                       _i32, _vp, _vp, _vp]),
     "psw_vup_projection": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "psw_lse_combine_vup": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _i32, _vp, _vp,
+                                   _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "psw_tile_bounds": (_i32, [ctypes.POINTER(PswAttnArgs), _i32, _i32, _i32, _vp, _vp, _i32,
                                _vp, _vp]),
     "psw_debug_take_failures": (_i32, [ctypes.POINTER(ctypes.c_uint32)]),

@@ -504,6 +504,42 @@ int psw_vup_projection(const void* x, const void* w_uv, void* out, int32_t num_t
                    "vup_projection");
 }
 
+int psw_lse_combine_vup(const void* const* partial_out, const float* const* partial_lse,
+                        int32_t num_partials, int32_t partial_dtype, const void* w_uv,
+                        void* out, float* out_lse, void* merged, int32_t num_tokens,
+                        int32_t num_heads, int32_t kv_lora_rank, int32_t v_head_dim,
+                        void* stream) {
+  const int max_p = psw::combine_vup_max_partials();
+  if (num_partials < 1 || num_partials > max_p)
+    return fail(PSW_ERR_INVALID, "num_partials %d outside [1, %d]", num_partials, max_p);
+  if (num_tokens < 0 || num_heads < 0 || kv_lora_rank < 1 || v_head_dim < 1)
+    return fail(PSW_ERR_INVALID, "num_tokens %d, num_heads %d, kv_lora_rank %d, v_head_dim %d",
+                num_tokens, num_heads, kv_lora_rank, v_head_dim);
+  if (!known_dtype(partial_dtype))
+    return fail(PSW_ERR_INVALID, "unknown partial dtype %d", partial_dtype);
+  if (!psw::vup_supported(kv_lora_rank, v_head_dim))
+    return fail(PSW_ERR_UNSUPPORTED, "kv_lora_rank %d / v_head_dim %d (need 128, 256 or 512 / a "
+                "multiple of 64)", kv_lora_rank, v_head_dim);
+  const bool work = num_tokens > 0 && num_heads > 0;
+  if (work && (partial_out == nullptr || partial_lse == nullptr))
+    return fail(PSW_ERR_INVALID, "partial pointer arrays are required");
+  psw::CombineArgs parts{};
+  for (int i = 0; work && i < num_partials; ++i) {
+    if (partial_out[i] == nullptr || partial_lse[i] == nullptr)
+      return fail(PSW_ERR_INVALID, "partial %d is NULL", i);
+    parts.out[i] = partial_out[i];
+    parts.lse[i] = partial_lse[i];
+  }
+  if (work && (w_uv == nullptr || out == nullptr))
+    return fail(PSW_ERR_INVALID, "w_uv and out are required");
+  return check_hip(psw::launch_combine_vup(parts, num_partials, partial_dtype,
+                                           static_cast<const uint16_t*>(w_uv),
+                                           static_cast<uint16_t*>(out), out_lse,
+                                           static_cast<uint16_t*>(merged), num_tokens, num_heads,
+                                           kv_lora_rank, v_head_dim, (hipStream_t)stream),
+                   "lse_combine_vup");
+}
+
 int psw_debug_take_failures(uint32_t* mask) {
   if (mask == nullptr) return fail(PSW_ERR_INVALID, "mask is NULL");
   *mask = 0;

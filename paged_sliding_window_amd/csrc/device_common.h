@@ -115,6 +115,29 @@ __device__ __forceinline__ void store_out4(void* base, int64_t elem, int dtype, 
     *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(base) + elem) = to_bf16x4(a0, a1, a2, a3);
 }
 
+// Eight consecutive elements of a partial, widened to fp32.
+template <int PART>
+__device__ __forceinline__ void load8(const void* base, int64_t elem, float (&v)[8]) {
+  if constexpr (PART == kOutF32) {
+    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+    const float4 a = src[0], b = src[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else if constexpr (PART == kOutF16) {
+    const f16x8 h = *reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(base) + elem);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (float)h[j];
+  } else {
+    const uint4 u4 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+    const uint32_t u[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __builtin_bit_cast(float, u[j] << 16);
+      v[2 * j + 1] = __builtin_bit_cast(float, u[j] & 0xffff0000u);
+    }
+  }
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
@@ -134,6 +157,8 @@ __device__ __forceinline__ void lds_barrier() {
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (expcnt and lgkmcnt left alone).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// s_waitcnt operand waiting for LDS / scalar-memory operations only (lgkmcnt <= n)
+constexpr int waitcnt_lgkm(int n) { return 0xF | (0x7 << 4) | ((n & 0xF) << 8) | (0x3 << 14); }
 
 __device__ __forceinline__ int load_uniform_i32(const int32_t* ptr) {
   return *(const __attribute__((address_space(4))) int32_t*)ptr;

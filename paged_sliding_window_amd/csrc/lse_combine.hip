@@ -15,29 +15,6 @@ namespace psw {
 
 constexpr int kCombineWaves = 4;
 
-// Eight consecutive elements of a partial, widened to fp32.
-template <int PART>
-__device__ __forceinline__ void load8(const void* base, int64_t elem, float (&v)[8]) {
-  if constexpr (PART == kOutF32) {
-    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
-    const float4 a = src[0], b = src[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else if constexpr (PART == kOutF16) {
-    const f16x8 h = *reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(base) + elem);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = (float)h[j];
-  } else {
-    const uint4 u4 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
-    const uint32_t u[4] = {u4.x, u4.y, u4.z, u4.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = __builtin_bit_cast(float, u[j] << 16);
-      v[2 * j + 1] = __builtin_bit_cast(float, u[j] & 0xffff0000u);
-    }
-  }
-}
-
 template <int PART, int OUT>
 __global__ __launch_bounds__(kCombineWaves * kWave) void lse_combine_kernel(
     const CombineArgs parts, int num_partials, int64_t num_rows, int head_dim_v,

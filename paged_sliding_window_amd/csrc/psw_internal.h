@@ -65,6 +65,13 @@ hipError_t launch_lse_combine(const CombineArgs& parts, int num_partials, int pa
 
 // V-up projection: out[t, h, :] = x[t, h, :] @ w[h] (bf16 in and out, fp32 accumulation).
 bool vup_supported(int kv_lora_rank, int v_head_dim);
+// LSE combine of P <= combine_vup_max_partials() latent partials followed by the
+// V-up projection, in one launch (merged rows optional, LSEs optional).
+int combine_vup_max_partials();
+hipError_t launch_combine_vup(const CombineArgs& parts, int num_partials, int partial_dtype,
+                              const uint16_t* w, uint16_t* out, float* out_lse, uint16_t* merged,
+                              int num_tokens, int num_heads, int kv_lora_rank, int v_head_dim,
+                              hipStream_t stream);
 hipError_t launch_vup_projection(const uint16_t* x, const uint16_t* w, uint16_t* out,
                                  int num_tokens, int num_heads, int kv_lora_rank, int v_head_dim,
                                  hipStream_t stream);

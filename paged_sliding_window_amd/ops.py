@@ -480,6 +480,52 @@ def vup_projection(x: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tens
     return out
 
 
+def lse_combine_vup(partial_outs: Sequence[torch.Tensor], partial_lses: Sequence[torch.Tensor],
+                    w_uv: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    out_lse: Optional[torch.Tensor] = None, merged: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """psw_lse_combine_vup: merge P partials [T, H, R] (or [T * H, R]; bf16, fp16 or
+    fp32, with lse [T, H] fp32) by LSE and project the merged rows with w_uv bf16
+    [H, R, Dv] in one launch -> out bf16 [T, H, Dv]; out_lse [T * H] fp32 and the
+    merged rows bf16 [T * H, R] are written when given."""
+    _need(w_uv, "w_uv", torch.bfloat16, 3)
+    H, R, Dv = w_uv.shape
+    P = len(partial_outs)
+    if P != len(partial_lses) or P == 0:
+        raise ValueError("need as many LSE tensors as partial outputs, at least one")
+    pdt = partial_outs[0].dtype
+    for i, (o, l) in enumerate(zip(partial_outs, partial_lses)):
+        _need(o, f"partial_outs[{i}]", pdt)
+        _need(l, f"partial_lses[{i}]", torch.float32)
+    rows = partial_outs[0].numel() // R if R > 0 else 0
+    if rows * R != partial_outs[0].numel() or rows % H != 0 or partial_outs[0].shape[-1] != R:
+        raise ValueError(f"partials {tuple(partial_outs[0].shape)} do not match w_uv "
+                         f"{tuple(w_uv.shape)}")
+    for o, l in zip(partial_outs, partial_lses):
+        if o.numel() != rows * R or l.numel() != rows:
+            raise ValueError("partials disagree in size")
+    T = rows // H
+    if out is None:
+        out = torch.empty((T, H, Dv), dtype=torch.bfloat16, device=w_uv.device)
+    _need(out, "out", torch.bfloat16)
+    if out.numel() != T * H * Dv:
+        raise ValueError("out must hold num_tokens * num_heads * v_head_dim elements")
+    if out_lse is not None:
+        _need(out_lse, "out_lse", torch.float32)
+        if out_lse.numel() != rows:
+            raise ValueError("out_lse must hold num_tokens * num_heads elements")
+    if merged is not None:
+        _need(merged, "merged", torch.bfloat16)
+        if merged.numel() != rows * R:
+            raise ValueError("merged must hold num_tokens * num_heads * kv_lora_rank elements")
+    po = (ctypes.c_void_p * P)(*[o.data_ptr() for o in partial_outs])
+    pl = (ctypes.c_void_p * P)(*[l.data_ptr() for l in partial_lses])
+    check(load().psw_lse_combine_vup(po, pl, P, _dtype_code(pdt, "partial dtype"), _ptr(w_uv),
+                                     _ptr(out), _ptr(out_lse), _ptr(merged), T, H, R, Dv,
+                                     _stream(stream)))
+    return out
+
+
 def tile_bounds(query_start_loc: torch.Tensor, seq_lens: torch.Tensor,
                 mm_ranges: Optional[torch.Tensor], *, num_q_heads: int, num_kv_heads: int,
                 window: int, causal: bool, chunk_size: int, chunk_lookback: int, tile_size: int,

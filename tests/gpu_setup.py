@@ -106,7 +106,8 @@ class DecodeStep:
     library's slot mapping and KV write; one step is then
       slot mapping of the new token -> latent KV write -> ONE attention call
       whose key ranges are the history splits followed by the current key
-      (S + 1 partials, each with its LSE) -> LSE combine -> V-up projection.
+      (S + 1 partials, each with its LSE) -> LSE combine and V-up projection
+      (one launch by default, or the two launches).
     """
 
     def __init__(self, w, partial_dtype=torch.bfloat16, dv_up=128, wuv_seed=55):
@@ -165,9 +166,17 @@ class DecodeStep:
     def combine(self):
         psw.lse_combine(self.outs, self.lses, out=self.out, out_lse=self.out_lse)
 
-    def run(self, ev=None):
+    def combine_vup(self):
+        """The combine and the V-up projection in one launch (merged rows and
+        their LSEs written too)."""
+        psw.lse_combine_vup([self.part_o[j] for j in range(self.P)],
+                            [self.part_l[j] for j in range(self.P)], self.w_uv, out=self.vup_out,
+                            out_lse=self.out_lse, merged=self.out)
+
+    def run(self, ev=None, fused_tail=True):
         """One step; ev = 4 events recorded before the attention, after it, after
-        the combine and after the projection (or None)."""
+        the combine and after the projection (or None).  fused_tail: the combine
+        and the projection as one launch (the last two events then coincide)."""
         w = self.w
         psw.slot_mapping(self.qsl, self.positions, self.bt, w.block_size, w.num_seqs,
                          out=self.slots)
@@ -177,6 +186,12 @@ class DecodeStep:
         self.attention()
         if ev is not None:
             ev[1].record()
+        if fused_tail and self.P <= 16:   # the one-launch tail takes up to 16 partials
+            self.combine_vup()
+            if ev is not None:
+                ev[2].record()
+                ev[3].record()
+            return
         self.combine()
         if ev is not None:
             ev[2].record()

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     lib = psw.load()
-    assert lib.psw_abi_version() == 7
+    assert lib.psw_abi_version() == 8
     assert lib.psw_status_string(PSW_OK) == b"ok"
     assert lib.psw_status_string(PSW_ERR_INVALID) == b"invalid argument"
 
@@ -114,6 +114,23 @@ def test_other_entry_points_reject_bad_scalars():
     assert lib.psw_lse_combine(po, po, 65, 0, 1, 64, None, 0, None, None) == PSW_ERR_INVALID
     assert lib.psw_lse_combine(po, po, 1, 0, 1, 12, None, 0, None, None) == PSW_ERR_INVALID
     assert lib.psw_tile_bounds(ctypes.byref(_args()), 0, 16, 8, None, None, 0, None, None) == PSW_ERR_INVALID
+
+
+def test_combine_vup_host_checks():
+    # every case fails (or has no work) on the host: no pointer is dereferenced
+    lib = psw.load()
+    po = (ctypes.c_void_p * 17)()
+    f = lib.psw_lse_combine_vup
+    assert f(po, po, 0, 0, None, None, None, None, 1, 1, 512, 128, None) == PSW_ERR_INVALID
+    assert f(po, po, 17, 0, None, None, None, None, 1, 1, 512, 128, None) == PSW_ERR_INVALID
+    assert f(po, po, 2, 3, None, None, None, None, 1, 1, 512, 128, None) == PSW_ERR_INVALID
+    assert f(po, po, 2, 0, None, None, None, None, -1, 1, 512, 128, None) == PSW_ERR_INVALID
+    assert f(po, po, 2, 0, None, None, None, None, 1, 1, 96, 128, None) == PSW_ERR_UNSUPPORTED
+    assert f(po, po, 2, 0, None, None, None, None, 1, 1, 512, 96, None) == PSW_ERR_UNSUPPORTED
+    # NULL partials with work to do
+    assert f(po, po, 2, 0, None, None, None, None, 1, 1, 512, 128, None) == PSW_ERR_INVALID
+    # no tokens: nothing to do, nothing launched
+    assert f(po, po, 2, 0, None, None, None, None, 0, 1, 512, 128, None) == PSW_OK
 
 
 def _latent_decode_args(**kw):
