@@ -248,7 +248,9 @@ typedef struct psw_attn_args {
  * block is the unit of work), each query block's tile interval [lo, hi) is cut
  * into num_splits pieces of ceil((hi - lo) / num_splits) tiles, split s taking
  * the s-th (possibly empty); query blocks are 128 rows (128 / (num_q_heads /
- * num_kv_heads) positions of one request, rounded down) and tiles 32 keys.  Either way each
+ * num_kv_heads) positions of one request, rounded down) and tiles 32 keys, or 64
+ * keys at head dim 128 when a row spans more than 1,536 keys (window <= 0, or
+ * causal == 0 with window >= 769).  Either way each
  * split writes its partial output and LSE (-inf and a zero row where the split
  * sees no allowed key), and psw_lse_combine over the splits gives the unsplit
  * result.  Segmented splits serve the prefill shapes, whose work is one

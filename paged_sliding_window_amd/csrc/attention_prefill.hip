@@ -53,7 +53,7 @@
 
 namespace psw {
 
-template <int D, int WAVES, int STAGES>
+template <int D, int WAVES, int STAGES, int TILE = 32>
 struct PrefillShape {
   static constexpr int kD = D;
   static constexpr int kWaves = WAVES;
@@ -61,7 +61,13 @@ struct PrefillShape {
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kRowsPerWave = 32;
   static constexpr int kBlockM = kWaves * kRowsPerWave;
-  static constexpr int kTile = 32;
+  static constexpr int kTile = TILE;       // keys per tile: 32, or 64 (two 32-key score blocks)
+  static constexpr int kKeyBlocks = kTile / 32;  // S^T accumulators of 32 keys
+  static constexpr int kKeyGroups = kTile / 16;  // 16-key k-steps of the output product
+  // 64-key tiles gather cached keys with one 64-bit address per lane (a lane's
+  // rows of a tile are consecutive keys inside one cache block) instead of the
+  // base + 32-bit offset form of 32-key tiles, whose rows lie in at most two blocks
+  static constexpr bool kLaneDma = kTile > 32;
   // LDS layout of a tile: one LDS-DMA instruction moves 1 KB = kRowsPerInstr
   // whole rows (rows g, g + kInstrPerTile, ...), written as one block; blocks
   // are kKBlock / kVBlock bytes apart.  The 16 extra bytes per K block put 16
@@ -80,7 +86,10 @@ struct PrefillShape {
   static constexpr int kLdsBytes = kStages * kBufBytes;
   static constexpr int kQFrags = D / 16;   // MFMA k-steps of the score product
   static constexpr int kOBlocks = D / 32;  // 32-column output blocks
-  static constexpr int kPvSteps = 2 * kOBlocks;
+  static constexpr int kPvSteps = kKeyGroups * kOBlocks;
+  static_assert(kTile == 32 || kTile == 64, "tile of 32 or 64 keys");
+  static_assert(kKeyBlocks == 1 || 32 % kInstrPerTile == 0,
+                "the second score block's rows sit at a fixed offset from the first's");
   static_assert(kRowsPerInstr * D * 2 == 1024 && kInstrPerWave >= 1 &&
                     kInstrPerWave * kWaves == kInstrPerTile,
                 "tile rows must split evenly into LDS-DMA instructions and waves");
@@ -93,6 +102,15 @@ struct PrefillShape {
 template <class S>
 __host__ __device__ constexpr int lds_row(int r, int block_bytes) {
   return (r % S::kInstrPerTile) * block_bytes + (r / S::kInstrPerTile) * (1024 / S::kRowsPerInstr);
+}
+
+// LDS byte offset, from the lane's first K read, of the score product's c-th
+// K read: k-chunk c % kQFrags (16 columns, 32 bytes) of key block c / kQFrags
+// (rows 32 kb + [0, 32), a fixed distance from block 0's rows).
+template <class S>
+__host__ __device__ constexpr int k_read_offset(int c) {
+  return (c / S::kQFrags) * (lds_row<S>(32 % S::kTile, S::kKBlock) - lds_row<S>(0, S::kKBlock)) +
+         (c % S::kQFrags) * 32;
 }
 
 __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_dst) {
@@ -281,6 +299,8 @@ prefill_attention_kernel(const AttnParams p) {
       bool fast;
       const char* kb;  // uniform K and V bases of this wave's first instruction
       const char* vb;
+      const char* ka;  // 64-key tiles: this lane's K and V addresses for that instruction
+      const char* va;
     };
     const int64_t wave_row = (int64_t)wave * S::kInstrPerWave * pitch;
     auto plan_tile = [&](int tile) __attribute__((always_inline)) {
@@ -296,11 +316,38 @@ prefill_attention_kernel(const AttnParams p) {
                    (int64_t)(S::kTile + S::kInstrPerTile) * pitch + 1024 < ((int64_t)1 << 31);
           d.kb = knew + (d.lo + wave_row);
           d.vb = vnew + (d.lo + wave_row);
+          if constexpr (S::kLaneDma) {
+            d.ka = d.kb + d.voff;
+            d.va = d.vb + d.voff;
+          }
           return d;
         }
         if (first + S::kTile > ctx) return d;  // old and new keys: per-lane path
       }
       if (!fast_blocks) return d;
+      if constexpr (S::kLaneDma) {
+        // A lane's rows of the tile are keys first + rq + g, g < kInstrPerTile:
+        // consecutive keys that sit in one block when blocks hold at least
+        // kInstrPerTile keys (tiles start on multiples of 64).  The lane's
+        // address is its block's entry (one of the tile's kRowsPerInstr row
+        // groups, picked from uniform table reads) plus its row and chunk.
+        if ((1 << bs_log2) < S::kInstrPerTile) return d;
+        const int bf = first >> bs_log2, bl = (first + S::kTile - 1) >> bs_log2;
+        if (bf < blk0 || bl - blk0 >= 128) load_window(bf);
+        int e = 0;
+        static_for<S::kRowsPerInstr>([&](auto qq) {
+          constexpr int q = decltype(qq)::value;
+          const int eq = entry(((first + q * S::kInstrPerTile) >> bs_log2) - blk0);
+          e = dma_q == q ? eq : e;
+        });
+        PSW_DCHECK(1, first + S::kTile > seq_len || e >= 0);
+        d.fast = first + S::kTile <= seq_len;
+        const int64_t row =
+            ((int64_t)e << bs_log2) + ((first + rq) & bs_mask) + wave * S::kInstrPerWave;
+        d.ka = kbase + (row * pitch + dma_ch * 16);
+        d.va = vbase + (row * pitch + dma_ch * 16);
+        return d;
+      }
       // with 16-key blocks keys [first, first + 16) sit in block b and the
       // rest in b + 1; larger blocks hold the whole tile
       const int b = first >> bs_log2;
@@ -329,13 +376,15 @@ prefill_attention_kernel(const AttnParams p) {
     const uint32_t pitch32 = (uint32_t)pitch;
     auto dma_k = [&](const DmaPlan& d, int buf, int i) __attribute__((always_inline)) {
       const int g = wave * S::kInstrPerWave + i;
-      lds_dma16(d.kb + (uint32_t)(d.voff + (uint32_t)i * pitch32),
-                smem + buf * S::kBufBytes + g * S::kKBlock);
+      char* dst = smem + buf * S::kBufBytes + g * S::kKBlock;
+      if constexpr (S::kLaneDma) lds_dma16(d.ka + (int64_t)i * pitch, dst);
+      else lds_dma16(d.kb + (uint32_t)(d.voff + (uint32_t)i * pitch32), dst);
     };
     auto dma_v = [&](const DmaPlan& d, int buf, int i) __attribute__((always_inline)) {
       const int g = wave * S::kInstrPerWave + i;
-      lds_dma16(d.vb + (uint32_t)(d.voff + (uint32_t)i * pitch32),
-                smem + buf * S::kBufBytes + S::kKBytes + g * S::kVBlock);
+      char* dst = smem + buf * S::kBufBytes + S::kKBytes + g * S::kVBlock;
+      if constexpr (S::kLaneDma) lds_dma16(d.va + (int64_t)i * pitch, dst);
+      else lds_dma16(d.vb + (uint32_t)(d.voff + (uint32_t)i * pitch32), dst);
     };
     auto issue_tile = [&](int tile, int buf, const DmaPlan& d) __attribute__((always_inline)) {
       char* kt = smem + buf * S::kBufBytes;
@@ -374,9 +423,9 @@ prefill_attention_kernel(const AttnParams p) {
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // bf16 column in a 32-block
     const uint32_t k_lane = (uint32_t)(lds_row<S>(lane & 31, S::kKBlock) + half * 16);
     const uint32_t v_lane = (uint32_t)(S::kKBytes + tr_col * 2);
-    uint32_t v_rows[2][2];
+    uint32_t v_rows[S::kKeyGroups][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < S::kKeyGroups; ++j) {
       v_rows[j][0] = v_lane + (uint32_t)lds_row<S>(16 * j + tr_row, S::kVBlock);
       v_rows[j][1] = v_lane + (uint32_t)lds_row<S>(16 * j + tr_row + 8, S::kVBlock);
     }
@@ -423,26 +472,29 @@ prefill_attention_kernel(const AttnParams p) {
       }
       const uint32_t kt = smem0 + (uint32_t)(buf * S::kBufBytes);
 
-      // S^T[key][row] for the 32 keys; K k-chunks read KA ahead.  Two copies
-      // of the sequence, with and without the DMA of tile tn, so that no
-      // branch sits between the MFMAs.
-      f32x16 s;
+      // S^T[key][row] for each 32-key block of the tile (its own accumulator);
+      // MFMA c reads k-chunk c % kQFrags of key block c / kQFrags, K reads
+      // KA ahead.  Two copies of the sequence, with and without the DMA of
+      // tile tn, so that no branch sits between the MFMAs.
+      f32x16 s[S::kKeyBlocks];
       auto score = [&](auto with_dma) __attribute__((always_inline)) {
         constexpr bool DMA = decltype(with_dma)::value;
-        constexpr int N = S::kQFrags, KA = 3;
+        constexpr int NQ = S::kQFrags, N = NQ * S::kKeyBlocks, KA = 3;
         const uint32_t ka = kt + k_lane;
         bf16x8 kf[KA + 1];
         static_for<KA>([&](auto cc) {
           constexpr int c = decltype(cc)::value;
-          kf[c] = lds_read_b128_at<c * 32>(ka);
+          kf[c] = lds_read_b128_at<k_read_offset<S>(c)>(ka);
         });
-        s = f32x16{};
+#pragma unroll
+        for (int kb = 0; kb < S::kKeyBlocks; ++kb) s[kb] = f32x16{};
         static_for<N>([&](auto cc) {
           constexpr int c = decltype(cc)::value;
           constexpr int issued = c + KA < N ? c + KA : N;
           lds_wait<issued - 1 - c>(kf[c % (KA + 1)]);
-          s = mfma32(kf[c % (KA + 1)], qf[c], s);
-          if constexpr (c + KA < N) kf[(c + KA) % (KA + 1)] = lds_read_b128_at<(c + KA) * 32>(ka);
+          s[c / NQ] = mfma32(kf[c % (KA + 1)], qf[c % NQ], s[c / NQ]);
+          if constexpr (c + KA < N)
+            kf[(c + KA) % (KA + 1)] = lds_read_b128_at<k_read_offset<S>(c + KA)>(ka);
           constexpr int step = N / S::kInstrPerWave;
           if constexpr (DMA && c % step == 0) dma_k(nd, bn, c / step);
           if constexpr (DMA && c % step == step / 2) dma_v(nd, bn, c / step);
@@ -452,14 +504,19 @@ prefill_attention_kernel(const AttnParams p) {
       else score(std::false_type{});
       if (!(base >= wave_lo && base + S::kTile - 1 <= wave_hi)) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int k = base + (i / 4) * 8 + half * 4 + (i % 4);
-          s[i] = (k >= row_lo && k <= row_hi) ? s[i] : -INFINITY;
-        }
-      }
-      float mx = s[0];
+        for (int kb = 0; kb < S::kKeyBlocks; ++kb)
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+          for (int i = 0; i < 16; ++i) {
+            const int k = base + 32 * kb + (i / 4) * 8 + half * 4 + (i % 4);
+            s[kb][i] = (k >= row_lo && k <= row_hi) ? s[kb][i] : -INFINITY;
+          }
+      }
+      float mx = s[0][0];
+#pragma unroll
+      for (int kb = 0; kb < S::kKeyBlocks; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kb > 0 || i > 0) mx = fmaxf(mx, s[kb][i]);
       mx = pair_max(mx) * c2;
       // move the running max only when it grows by more than 2^8
       if (__ballot(mx > m_run + 8.f) != 0) {
@@ -472,15 +529,24 @@ prefill_attention_kernel(const AttnParams p) {
         m_run = m_new;
       }
       const float m_sub = m_run == -INFINITY ? 0.f : m_run;
+      // P^T in bf16, one B operand per 16-key group: keys 16 j + [0, 16) are
+      // elements 8 (j % 2) .. + 8 of key block j / 2's accumulator
+      bf16x8 pf[S::kKeyGroups];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = fast_exp2(fmaf(s[i], c2, -m_sub));
-      const bf16x8 pf0 = to_bf16x8(s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]);
-      const bf16x8 pf1 = to_bf16x8(s[8], s[9], s[10], s[11], s[12], s[13], s[14], s[15]);
+      for (int kb = 0; kb < S::kKeyBlocks; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(fmaf(s[kb][i], c2, -m_sub));
+        pf[2 * kb] = to_bf16x8(s[kb][0], s[kb][1], s[kb][2], s[kb][3], s[kb][4], s[kb][5],
+                               s[kb][6], s[kb][7]);
+        pf[2 * kb + 1] = to_bf16x8(s[kb][8], s[kb][9], s[kb][10], s[kb][11], s[kb][12],
+                                   s[kb][13], s[kb][14], s[kb][15]);
+      }
       // row sum over the bf16 probabilities the output product uses
       static_for<4>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
-        l_run = dot2_bf16(__builtin_shufflevector(pf0, pf0, 2 * i, 2 * i + 1), ones, l_run);
-        l_run = dot2_bf16(__builtin_shufflevector(pf1, pf1, 2 * i, 2 * i + 1), ones, l_run);
+#pragma unroll
+        for (int j = 0; j < S::kKeyGroups; ++j)
+          l_run = dot2_bf16(__builtin_shufflevector(pf[j], pf[j], 2 * i, 2 * i + 1), ones, l_run);
       });
 
       // O^T += V^T P^T: step st covers output columns b*32 + [0, 32) and keys
@@ -501,7 +567,7 @@ prefill_attention_kernel(const AttnParams p) {
           constexpr int issued = st + VA < N ? st + VA : N;
           lds_wait<2 * (issued - 1 - st)>(vr[st % (VA + 1)][0], vr[st % (VA + 1)][1]);
           o[st % S::kOBlocks] = mfma32(cat8(vr[st % (VA + 1)][0], vr[st % (VA + 1)][1]),
-                                       st / S::kOBlocks == 0 ? pf0 : pf1, o[st % S::kOBlocks]);
+                                       pf[st / S::kOBlocks], o[st % S::kOBlocks]);
           if constexpr (st + VA < N) read_v(std::integral_constant<int, st + VA>{});
         });
       }
@@ -592,14 +658,8 @@ bool prefill_supported(int head_dim_qk, int head_dim_v, int queries_per_kv, bool
 // 8-wave workgroup per CU with a four-deep ring (prefetch distance three
 // tiles) measured no faster on the 16,550-token workload: the tile loads are
 // not what the loop waits for.
-template <int D> struct PrefillConfig;
-template <> struct PrefillConfig<64> { using S = PrefillShape<64, 4, 2>; };
-template <> struct PrefillConfig<128> { using S = PrefillShape<128, 4, 2>; };
-template <> struct PrefillConfig<256> { using S = PrefillShape<256, 4, 2>; };
-
-template <int D, bool FUSED>
+template <class S, bool FUSED>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
-  using S = typename PrefillConfig<D>::S;
   const int block_q = S::kBlockM / p.queries_per_kv;
   const int gx = p.num_tokens / block_q + p.num_seqs;
   if (gx == 0) return hipSuccess;
@@ -613,12 +673,31 @@ static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Head dim 128 takes 64-key tiles when a query row spans more than 1,536 keys
+// (no window, or a non-causal window of 769 or more): a tile's fixed work (its
+// barrier, DMA plan, row-max exchange and rescale test) is then spread over
+// twice the MFMAs (the 2 x 4096-token non-causal workload with W 1024: 0.079
+// against 0.091 ms).  Shorter rows keep 32-key tiles: a 64-key tile wastes
+// more keys at the window's edges, and its registers allow two resident
+// workgroups per CU instead of three (the chunked W 512 workload: 0.056
+// against 0.052 ms; a causal W 1024 one: equal).  The choice depends only on
+// the call's mask geometry, so a call and its fused-write twin tile alike.
+bool prefill_long_tiles(int head_dim, int window, int causal) {
+  if (head_dim != 128) return false;
+  if (window <= 0) return true;
+  const int64_t span = causal ? (int64_t)window : 2 * (int64_t)window - 1;
+  return span > 1536;
+}
+
 template <bool FUSED>
 static hipError_t launch_prefill_d(const AttnParams& p, hipStream_t stream) {
   switch (p.head_dim_qk) {
-    case 64: return launch_prefill_t<64, FUSED>(p, stream);
-    case 128: return launch_prefill_t<128, FUSED>(p, stream);
-    case 256: return launch_prefill_t<256, FUSED>(p, stream);
+    case 64: return launch_prefill_t<PrefillShape<64, 4, 2>, FUSED>(p, stream);
+    case 128:
+      if (prefill_long_tiles(128, p.geom.window, p.geom.causal))
+        return launch_prefill_t<PrefillShape<128, 4, 2, 64>, FUSED>(p, stream);
+      return launch_prefill_t<PrefillShape<128, 4, 2>, FUSED>(p, stream);
+    case 256: return launch_prefill_t<PrefillShape<256, 4, 2>, FUSED>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

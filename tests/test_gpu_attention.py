@@ -134,8 +134,8 @@ def test_segmented_splits_partials_and_combine(seed):
     """Segmented splits: each query block's tile loop cut into S pieces.  Every
     piece must equal the oracle over exactly its keys (the block's tile
     interval from the oracle's tile bounds at the kernel's tiling: 128-row
-    blocks, 32-key tiles), and the LSE combine of the S pieces the unsplit
-    attention."""
+    blocks, 32- or 64-key tiles), and the LSE combine of the S pieces the
+    unsplit attention."""
     import paged_sliding_window_amd as psw
     from oracle import tile_bounds_ref
     rng = np.random.default_rng(900 + seed)
@@ -155,7 +155,10 @@ def test_segmented_splits_partials_and_combine(seed):
     parts, lses = parts.cpu().numpy(), lses.cpu().numpy()
     merged = merged.cpu().numpy().reshape(N, Hq, d)
     merged_lse = merged_lse.cpu().numpy().reshape(N, Hq)
-    block_q, T = 128 // qpk, 32
+    # the kernel's tiling (include/psw.h, segmented splits): 64-key tiles at head
+    # dim 128 when a row spans more than 1,536 keys
+    span = (1 << 30) if w.window <= 0 else (w.window if w.causal else 2 * w.window - 1)
+    block_q, T = 128 // qpk, 64 if d == 128 and span > 1536 else 32
     use_mm = w.max_mm_ranges > 0 and (w.mm_ranges != 0).any()
     for r in range(w.num_seqs):
         s0, ql = int(w.query_start_loc[r]), int(w.query_lens[r])
