@@ -5,11 +5,13 @@
 // each wave owns 64 x kSlotTokensPerThread consecutive tokens, finds the
 // request of its first token with a 64-way search over query_start_loc (each
 // round one load per lane and a ballot, two rounds for 4096 requests); each
-// lane then moves to its own first token's request (one step for the usual
-// case of one boundary, a galloping search when many short requests lie in
-// between, as in decode batches of one token per request) and crosses the
-// boundaries inside its own tokens with the next few boundaries read ahead.  Positions are read with 16-byte loads and slots (or -1) written
-// with 16-byte stores, so every wave streams contiguous positions and slots.
+// lane then finds its own first token's request among the 64 boundaries that
+// follow, loaded one per lane and searched across the lanes (many short
+// requests per wave, as in decode batches of one token per request), or
+// beyond them by a galloping search, and crosses the boundaries inside its own
+// tokens with the next few boundaries read ahead.  Positions are read with
+// 16-byte loads and slots (or -1) written with 16-byte stores, so every wave
+// streams contiguous positions and slots.
 // Block-table entries are read per token; consecutive tokens of a request hit
 // the same cache line, which plays the role of the page's bounded window.
 #include <type_traits>
@@ -19,16 +21,10 @@
 namespace psw {
 
 constexpr int kSlotThreads = 256;
-#ifndef SLOT_TPT
-#define SLOT_TPT 8
-#endif
-constexpr int kSlotTokensPerThread = SLOT_TPT;  // a multiple of 4
+constexpr int kSlotTokensPerThread = 8;  // a multiple of 4
 static_assert(kSlotTokensPerThread % 4 == 0, "whole 16-byte stores");
 constexpr int kWaveLanes = 64;
-#ifndef SLOT_CHUNKS
-#define SLOT_CHUNKS 1
-#endif
-constexpr int kSlotChunks = SLOT_CHUNKS;  // consecutive chunks of 64 x kSlotTokensPerThread per wave
+constexpr int kSlotChunks = 1;  // consecutive chunks of 64 x kSlotTokensPerThread per wave
 
 // Largest r in [0, num_reqs) with qsl[r] <= t (qsl non-decreasing, qsl[0] = 0
 // <= t): the candidate interval shrinks 64-fold per round, every lane testing
