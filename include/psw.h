@@ -273,7 +273,7 @@ int psw_swa_mm_attention(const psw_attn_args* args, void* stream);
  * one) is a scratch array inside the library instead of args->workspace, which
  * is ignored with workspace_bytes; the caller still passes inputs and outputs.
  * The call itself allocates nothing (no hipMalloc / hipFree).
- * Limit: the scratch holds 130 MiB on each device, enough for the latent decode
+ * Limit: the scratch holds 66 MiB on each device, enough for the latent decode
  * with up to 128 query heads per workgroup on 256 CUs and up to 458,751
  * (token, split) items; a call needing more fails with PSW_ERR_INVALID and a
  * message, before anything is enqueued.  Every device the library runs on holds its copy of the

@@ -93,7 +93,7 @@ hipError_t launch_attention_decode(const AttnParams& p, void* workspace, hipStre
 
 // Device scratch of the allocation-free entry point (one per device, this many
 // bytes): its address on the current device, looked up on first use.
-constexpr int64_t kScratchBytes = (int64_t)130 << 20;
+constexpr int64_t kScratchBytes = (int64_t)66 << 20;
 hipError_t scratch_device_ptr(void** ptr);
 
 // Failed debug checks recorded on the current device by each translation

@@ -292,7 +292,7 @@ def test_combine_shapes():
 @no_gpu_only
 def test_noalloc_rejects_calls_beyond_its_scratch():
     """The allocation-free entry point checks its workspace need against the
-    130 MiB scratch on the host: a latent decode of 4 tokens x 120,000 splits
+    66 MiB scratch on the host: a latent decode of 4 tokens x 120,000 splits
     (480,000 items) is refused before anything is launched, 4 x 100,000 fits;
     a prefill call needs no scratch."""
     lib = psw.load()
@@ -305,8 +305,8 @@ def test_noalloc_rejects_calls_beyond_its_scratch():
     n = ctypes.c_int64()
     ok = _latent_decode_args(num_splits=100000, **ptrs)
     assert lib.psw_attention_workspace_size(ctypes.byref(ok), ctypes.byref(n)) == PSW_OK
-    assert 0 < n.value <= 130 << 20
+    assert 0 < n.value <= 66 << 20
     assert lib.psw_attention_workspace_size(ctypes.byref(big), ctypes.byref(n)) == PSW_OK
-    assert n.value > 130 << 20
+    assert n.value > 66 << 20
     # the empty call is accepted with nothing to do
     assert lib.psw_swa_mm_attention_noalloc(ctypes.byref(_args()), None) == PSW_OK
