@@ -11,10 +11,11 @@ LSE combine, V-up projection) is timed in the same run and reported under
 lookback) under "prefill_configs".
 
 Reported value: algorithmic TFLOP/s = 4 * head_dim FLOP per allowed
-(query, key, head) triple over the measured step time.  The "roofline" object
-is for the dominant kernel (prefill attention), timed with HIP events around
-each of its launches on the stream it runs on, after a time-based warm-up that
-brings the clocks to their steady state.
+(query, key, head) triple over the measured step time (steps with no event
+recorded between their launches).  The "roofline" object is for the dominant
+kernel (prefill attention), timed over as many steps again with HIP events
+around each of its launches on the stream it runs on.  Every timed section
+follows a time-based warm-up that brings the clocks to their steady state.
 """
 from __future__ import annotations
 
@@ -333,14 +334,20 @@ def main():
     t1 = torch.cuda.Event(enable_timing=True)
 
     def time_steps(step):
-        """(ms per step, mean ms of the timed kernel) over args.steps steps."""
+        """(ms per step, mean ms of the timed kernel): args.steps steps with no
+        event recorded between their launches (each record costs a few
+        microseconds of the stream's time), then args.steps more with events
+        around the kernel."""
         t0.record()
-        for i in range(args.steps):
-            step(i)
+        for _ in range(args.steps):
+            step()
         t1.record()
         torch.cuda.synchronize()
-        return (t0.elapsed_time(t1) / args.steps,
-                sum(a.elapsed_time(b) for a, b in ev) / args.steps)
+        ms = t0.elapsed_time(t1) / args.steps
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        return ms, sum(a.elapsed_time(b) for a, b in ev) / args.steps
 
     log("timing prefill")
     for _ in range(args.warmup):
@@ -629,12 +636,18 @@ def bench_decode(args, torch, psw, np):
     warm_ms = warm(torch, ds.run, min_ms=args.warm_ms)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    # the step time with no event recorded between launches (four records per
+    # step add about 10 us of stream time), then the same steps with events
+    # around the attention call and the tail
     t0.record()
-    for i in range(steps):
-        ds.run(ev[i])
+    for _ in range(steps):
+        ds.run()
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
+    for i in range(steps):
+        ds.run(ev[i])
+    torch.cuda.synchronize()
     attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     tail_ms = sum(e[1].elapsed_time(e[3]) for e in ev) / steps
     kv_bytes = int(w.seq_lens.sum()) * w.head_dim_qk * 2
