@@ -36,7 +36,9 @@ __device__ __forceinline__ int find_request_wave(const int32_t* __restrict__ qsl
     const int step = (n + kWaveLanes - 1) / kWaveLanes;
     const int r = lo + lane * step;
     const bool ok = lane * step < n && qsl[r] <= t;
-    const uint64_t m = __ballot(ok);  // lane 0 tests qsl[lo] <= t: never empty
+    // lane 0 tests qsl[lo] <= t (qsl[0] = 0 <= t): never empty; the bit is
+    // forced so that a malformed qsl still keeps the search in range
+    const uint64_t m = __ballot(ok) | 1ull;
     const int k = 63 - __builtin_clzll(m);
     const int nlo = lo + k * step;
     n = min(step, lo + n - nlo);
@@ -162,17 +164,32 @@ __device__ __forceinline__ void slot_chunk(
   }
   // the wave's first token's request (uniform), searched once per wave, when
   // it has real tokens; later chunks continue from each lane's request
+  int32_t win[kSlotTokensPerThread];
+  bool have_win = false;  // win[] already holds this lane's next boundaries
   if (!have_r && num_reqs > 0 && wave_t0 < num_tokens) {
     // (uniform branch: every lane of the wave takes it)
-    r = find_request_wave(qsl, num_reqs, (int)wave_t0, lane);
-    // The 64 boundaries after it, one per lane, in one load: a lane whose
+    // The 64 boundaries after the wave's request, one per lane: a lane whose
     // first token lies within them finds its request by a binary search over
     // the lanes (the boundaries are non-decreasing), so batches of short
     // requests, such as decode steps of one token per request, need no chain
     // of dependent loads.  `next` is the first token of the request after the
     // lane's (kept in a register: read again only when a lane crosses into it).
-    const int wj = r + 1 + lane;
-    const int32_t wq = wj < num_reqs ? qsl[wj] : INT32_MAX;
+    int32_t wq;
+    const bool small = num_reqs <= kWaveLanes;
+    if (small) {
+      // At most 64 requests: every start in one load, qsl[lane]; the wave's
+      // request (the last start at or below its first token) by a ballot, and
+      // the boundaries after it by lane shuffles
+      const int32_t v = lane < num_reqs ? qsl[lane] : INT32_MAX;
+      r = 63 - __builtin_clzll(__ballot((int64_t)v <= wave_t0) | 1ull);
+      const int src = r + 1 + lane;
+      const int32_t sv = __shfl(v, min(src, kWaveLanes - 1), kWaveLanes);
+      wq = src < num_reqs ? sv : INT32_MAX;
+    } else {
+      r = find_request_wave(qsl, num_reqs, (int)wave_t0, lane);
+      const int wj = r + 1 + lane;
+      wq = wj < num_reqs ? qsl[wj] : INT32_MAX;
+    }
     int cnt = 0;  // boundaries of the window at or below t0 (a prefix of it)
 #pragma unroll
     for (int step = 32; step > 0; step >>= 1) {
@@ -185,6 +202,16 @@ __device__ __forceinline__ void slot_chunk(
     r += cnt;
     if (cnt < kWaveLanes) next = nx;
     else next = r + 1 < num_reqs ? qsl[r + 1] : INT32_MAX;  // past the window: read on
+    if (small) {
+      // the window holds every later boundary: the lane's next ones,
+      // qsl[r + 1 + k], are window lanes cnt + k (past the window: none)
+#pragma unroll
+      for (int k = 0; k < kSlotTokensPerThread; ++k) {
+        const int32_t x = __shfl(wq, min(cnt + k, kWaveLanes - 1), kWaveLanes);
+        win[k] = cnt + k < kWaveLanes ? x : INT32_MAX;
+      }
+      have_win = true;
+    }
     have_r = true;
   }
   // this lane's first token's request
@@ -221,20 +248,28 @@ __device__ __forceinline__ void slot_chunk(
       }
     }
   }
-  // General path: the lane's next boundaries qsl[rw + 1 + k], read together,
-  // serve its tokens' crossings (one token per request needs one per token);
-  // more crossings than that (empty requests) read on
-  int32_t win[kSlotTokensPerThread];
+  // General path: the lane's next boundaries qsl[rw + 1 + k], read together
+  // (or taken from the window above), serve its tokens' crossings (one token
+  // per request needs one per token); more crossings than that (empty
+  // requests) read on
   const int rw = r;
-  if (!done && num_reqs > 0 && t0 < num_tokens) {
+  PSW_DCHECK(16, !have_win || t0 >= num_tokens || t0 < next);
+  if (!done && num_reqs > 0 && t0 < num_tokens && !have_win) {
 #pragma unroll
     for (int k = 0; k < kSlotTokensPerThread; ++k)
       win[k] = rw + 1 + k < num_reqs ? qsl[rw + 1 + k] : INT32_MAX;
   }
+  // First each token's request and its table element (tix, -1 when the
+  // token maps to -1) with its offset inside the block, then the table
+  // entries of all the lane's tokens as one round of independent loads: a
+  // load per token inside the request walk would wait for each in turn (a
+  // decode batch of one token per request takes this path on every lane).
+  int64_t tix[kSlotTokensPerThread], toff[kSlotTokensPerThread];
 #pragma unroll
   for (int j = 0; j < kSlotTokensPerThread && !done; ++j) {
     const int64_t t = t0 + j;
-    res[j] = -1;
+    tix[j] = -1;
+    toff[j] = 0;
     if (t < num_tokens && num_reqs > 0) {
       while (t >= next) {  // crossing into the next request (empty ones skipped)
         ++r;
@@ -256,29 +291,36 @@ __device__ __forceinline__ void slot_chunk(
         if (p >= 0 && p <= INT32_MAX) {
           const uint32_t lb = (uint32_t)p >> g.bs_log2;
           if (lb < (uint32_t)stride) {
-            const int32_t b = block_table[(int64_t)r * stride + lb];
-            if (b >= 0)
-              res[j] = (int32_t)(((uint32_t)b << g.bs_log2) + ((uint32_t)p & (uint32_t)(block_size - 1)));
+            tix[j] = (int64_t)r * stride + lb;
+            toff[j] = (uint32_t)p & (uint32_t)(block_size - 1);
           }
         }
       } else if constexpr (MODE == kSlotPlain) {
         if (p >= 0) {
           const int64_t lb = p / block_size;
           if (lb < stride) {
-            const int32_t b = block_table[(int64_t)r * stride + lb];
-            if (b >= 0) res[j] = (int32_t)(b * (int64_t)block_size + (p - lb * block_size));
+            tix[j] = (int64_t)r * stride + lb;
+            toff[j] = p - lb * block_size;
           }
         }
       } else {
         uint32_t lb, off;
         if (p >= 0 && p <= INT32_MAX && cp_place<MODE, POW2>((uint32_t)p, g, lb, off) &&
             lb < (uint32_t)stride) {
-          // step 5: physical block through the table
-          const int32_t b = block_table[(int64_t)r * stride + lb];
-          if (b >= 0) res[j] = (int32_t)(b * (int64_t)block_size + off);
+          // step 5 below: physical block through the table
+          tix[j] = (int64_t)r * stride + lb;
+          toff[j] = off;
         }
       }
     }
+  }
+  if (!done) {
+    int32_t b[kSlotTokensPerThread];
+#pragma unroll
+    for (int j = 0; j < kSlotTokensPerThread; ++j) b[j] = tix[j] >= 0 ? block_table[tix[j]] : -1;
+#pragma unroll
+    for (int j = 0; j < kSlotTokensPerThread; ++j)
+      res[j] = b[j] >= 0 ? (int32_t)(b[j] * (int64_t)block_size + toff[j]) : -1;
   }
   if (t0 + kSlotTokensPerThread <= max_num_tokens && (((uintptr_t)(out + t0)) & 15) == 0) {
 #pragma unroll
