@@ -9,9 +9,12 @@
 // follow, loaded one per lane and searched across the lanes (many short
 // requests per wave, as in decode batches of one token per request), or
 // beyond them by a galloping search, and crosses the boundaries inside its own
-// tokens with the next few boundaries read ahead.  Positions are read with
-// 16-byte loads and slots (or -1) written with 16-byte stores, so every wave
-// streams contiguous positions and slots.
+// tokens with the next few boundaries read ahead.  With at most 64 requests
+// one load of query_start_loc (one start per lane) serves the search, the
+// window and the read-ahead through lane shuffles.  A lane's block-table
+// entries are loaded as one round after all its tokens' requests are known.
+// Positions are read with 16-byte loads and slots (or -1) written with
+// 16-byte stores, so every wave streams contiguous positions and slots.
 // Block-table entries are read per token; consecutive tokens of a request hit
 // the same cache line, which plays the role of the page's bounded window.
 #include <type_traits>
