@@ -148,9 +148,14 @@ __global__ __launch_bounds__(vup::kThreads) void combine_vup_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int half = lane >> 5;
   const int ncb = dv / kCols;
-  const int h = blockIdx.x / ncb, cb = blockIdx.x - h * ncb;
+  // the column blocks of one (head, token block) merge the same rows: give
+  // them neighbouring logical ids, which share an XCD and so its L2 (the
+  // second merge then reads the partials from L2 rather than HBM)
+  const int logical = xcd_logical_id(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int bx = logical % gridDim.x;
+  const int h = bx / ncb, cb = bx - h * ncb;
   const int64_t row_bytes = (int64_t)dv * 2;
-  const int tok0 = blockIdx.y * kTokens;
+  const int tok0 = (logical / gridDim.x) * kTokens;
 
   // W_UV[h][:, 64 cb .. + 64) -> LDS, as in vup_projection_kernel
   {
