@@ -147,6 +147,28 @@ def test_request_search_across_counts(R):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("R", [17, 64, 65])
+def test_runs_of_empty_requests(R):
+    """Most requests empty: a lane's few tokens cross dozens of boundaries,
+    past the eight it reads ahead (with at most 64 requests the boundaries
+    come from one load of the starts and lane shuffles, beyond 64 from the
+    request search)."""
+    rng = np.random.default_rng(500 + R)
+    B = 16
+    lens = np.zeros(R, dtype=np.int64)
+    lens[rng.choice(R, size=max(1, R // 8), replace=False)] = rng.integers(1, 20, size=max(1, R // 8))
+    lens[-1] = 0                      # trailing empty requests
+    stride = 4
+    bt = rng.integers(0, 9000, size=(R, stride)).astype(np.int32)
+    qsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    N = int(qsl[-1])
+    pos = rng.integers(0, stride * B, size=N).astype(np.int64)
+    M = N + 11
+    got = _gpu_slots(qsl, pos, bt, B, M)
+    ref = slot_mapping_ref(qsl, pos, bt, B, M)
+    assert np.array_equal(got, ref)
+
+
 @pytest.mark.parametrize("R", [64, 511, 4096])
 @pytest.mark.parametrize("B", [16, 64])
 def test_decode_shaped_batches(R, B):
